@@ -1,0 +1,268 @@
+// Device-side n-gram pool, candidate gather, greedy verification, window
+// slide and KV commit of one lookahead step.
+//
+// Pool ([LD] §3.4 "N-gram pool update": key = first token, value = list of
+// suffixes): direct-mapped by first token, V buckets of `cap` suffixes of
+// N-1 tokens, each bucket a FIFO ring (head = oldest).  An identical suffix is
+// skipped; a full bucket evicts its oldest entry.
+//
+// Gather ([LD] §3.4 "N-gram selection from the pool"): the bucket of the
+// current token, oldest first; the newest G if it holds more.
+//
+// Verify ([LD] §3.4 "Greedy verification algorithm (Algorithm 3)") as a
+// longest-prefix scan: candidate g's accepted length is the longest j with
+// cand[g][i-1] == argmax(row predicting position P+i) for all i <= j; the
+// first candidate with the longest match wins; the emitted tokens are its
+// accepted prefix plus the argmax that follows it (argmax of row 0 when
+// nothing is accepted), so every step emits 1..N tokens.
+#include "la_internal.h"
+
+namespace {
+
+__device__ __forceinline__ int32_t* bucket(const PoolDesc& p, int key, int e) {
+  return p.tok + ((size_t)key * p.cap + e) * p.n1;
+}
+
+struct InsertCounts {
+  int ins, dup, ev, ngr, keys;
+};
+
+// Insert (key, sfx[0..n1)) into the pool; one thread.
+__device__ void pool_insert(const PoolDesc& p, int key, const int32_t* sfx, InsertCounts& c) {
+  const int cnt = p.cnt[key];
+  const int head = p.head[key];
+  for (int e = 0; e < cnt; ++e) {
+    int idx = head + e;
+    if (idx >= p.cap) idx -= p.cap;
+    const int32_t* b = bucket(p, key, idx);
+    bool same = true;
+    for (int i = 0; i < p.n1; ++i) same = same && (b[i] == sfx[i]);
+    if (same) { ++c.dup; return; }
+  }
+  ++c.ins;
+  int idx;
+  if (cnt < p.cap) {
+    idx = head + cnt;
+    if (idx >= p.cap) idx -= p.cap;
+    p.cnt[key] = cnt + 1;
+    ++c.ngr;
+    if (cnt == 0) ++c.keys;
+  } else {
+    idx = head;
+    p.head[key] = head + 1 == p.cap ? 0 : head + 1;
+    ++c.ev;
+  }
+  int32_t* b = bucket(p, key, idx);
+  for (int i = 0; i < p.n1; ++i) b[i] = sfx[i];
+}
+
+__global__ __launch_bounds__(256) void k_gather(PoolDesc pool, StepIO io, RowLayout L) {
+  __shared__ int s_take, s_first;
+  DevState* st = io.st;
+  const int cur = st->cur, P = st->P;
+  const int n1 = L.N - 1;
+  if (threadIdx.x == 0) {
+    const int cnt = L.G > 0 ? pool.cnt[cur] : 0;
+    const int take = cnt < L.G ? cnt : L.G;
+    s_take = take;
+    int first = pool.head[cur] + (cnt - take);
+    if (first >= pool.cap) first -= pool.cap;
+    s_first = first;
+    st->ncand = take;
+    st->stats[ST_GATHER_NE] += take > 0;
+    st->stats[ST_CAND_TOTAL] += take;
+  }
+  __syncthreads();
+  const int take = s_take, first = s_first;
+  for (int u = threadIdx.x; u < L.G * n1; u += blockDim.x) {
+    const int g = u / n1, i = u - g * n1;
+    int v = 0;  // unused candidate slots hold token 0
+    if (g < take) {
+      int e = first + g;
+      if (e >= pool.cap) e -= pool.cap;
+      v = bucket(pool, cur, e)[i];
+    }
+    io.cand[u] = v;
+    io.ids[1 + L.W * n1 + u] = v;
+    io.pos[1 + L.W * n1 + u] = P + i + 1;
+  }
+  for (int u = threadIdx.x; u < L.W * n1; u += blockDim.x) {
+    const int l = u / L.W, k = u - l * L.W;
+    io.ids[1 + u] = io.win[u];
+    io.pos[1 + u] = P + 1 + l + k;
+  }
+  if (threadIdx.x == 0) {
+    io.ids[0] = cur;
+    io.pos[0] = P;
+  }
+}
+
+constexpr int VMAX_M = 2048;  // rows staged in LDS by the verify kernel
+
+__global__ __launch_bounds__(64) void k_verify(PoolDesc pool, StepIO io, RowLayout L) {
+  __shared__ int32_t a[VMAX_M];
+  __shared__ int32_t cand[VMAX_M];
+  __shared__ int32_t win[VMAX_M];
+  __shared__ int red[64][5];
+  DevState* st = io.st;
+  const int lane = threadIdx.x;
+  const int n1 = L.N - 1, W = L.W, G = L.G, M = L.M;
+  for (int i = lane; i < M; i += 64) a[i] = io.amax[i];
+  for (int i = lane; i < G * n1; i += 64) cand[i] = io.cand[i];
+  for (int i = lane; i < W * n1; i += 64) win[i] = io.win[i];
+  __syncthreads();
+
+  if (lane == 0) {
+    const int vbase = 1 + W * n1;
+    const int ncand = st->ncand;
+    int best = 0, bg = 0;
+    for (int g = 0; g < ncand; ++g) {
+      int acc = 0;
+      for (int i = 1; i <= n1; ++i) {
+        const int pred = i == 1 ? 0 : vbase + g * n1 + (i - 2);
+        if (cand[g * n1 + i - 1] != a[pred]) break;
+        acc = i;
+      }
+      if (acc > best) { best = acc; bg = g; }
+    }
+    const int bonus = best == 0 ? a[0] : a[vbase + bg * n1 + best - 1];
+    // commit: row 0 and the accepted candidate rows become cache rows P..P+best
+    st->commit_p = st->P;
+    st->commit_n = best + 1;
+    st->commit_rows[0] = 0;
+    for (int j = 1; j <= best; ++j) st->commit_rows[j] = vbase + bg * n1 + j - 1;
+    st->P += best + 1;
+    // emit, truncated to the budget; stop after EOS
+    const int room = io.max_new - st->total;
+    int n = 0, done = 0;
+    for (int j = 0; j <= best && n < room; ++j) {
+      const int tok = j < best ? cand[bg * n1 + j] : bonus;
+      st->out[n++] = tok;
+      if (io.eos >= 0 && tok == io.eos) { done = 1; break; }
+    }
+    st->n_out = n;
+    st->total += n;
+    if (st->total >= io.max_new) done = 1;
+    if (done) st->done = 1;
+    st->cur = bonus;
+    st->stats[ST_HIST0 + best] += 1;
+    st->stats[ST_STEPS] += 1;
+    st->stats[ST_TOKENS] += n;
+  }
+
+  // lookahead branch: harvest one n-gram per column (oldest level .. newest,
+  // then the column's new token) and insert in column order.  Columns sharing
+  // a first token are inserted by the lowest such column's lane, in order.
+  InsertCounts c = {0, 0, 0, 0, 0};
+  if (lane < W) {
+    const int key = win[lane];
+    bool leader = true;
+    for (int k2 = 0; k2 < lane; ++k2)
+      if (win[k2] == key) { leader = false; break; }
+    if (leader) {
+      int32_t sfx[LA_MAX_N];
+      for (int k2 = lane; k2 < W; ++k2) {
+        if (win[k2] != key) continue;
+        for (int l = 1; l < n1; ++l) sfx[l - 1] = win[l * W + k2];
+        sfx[n1 - 1] = a[1 + (n1 - 1) * W + k2];
+        pool_insert(pool, key, sfx, c);
+      }
+    }
+  }
+  red[lane][0] = c.ins; red[lane][1] = c.dup; red[lane][2] = c.ev;
+  red[lane][3] = c.ngr; red[lane][4] = c.keys;
+  __syncthreads();
+  if (lane == 0) {
+    long long t[5] = {0, 0, 0, 0, 0};
+    for (int i = 0; i < 64; ++i)
+      for (int j = 0; j < 5; ++j) t[j] += red[i][j];
+    st->stats[ST_INSERTS] += t[0];
+    st->stats[ST_DUPS] += t[1];
+    st->stats[ST_EVICT] += t[2];
+    st->stats[ST_NGRAMS] += t[3];
+    st->stats[ST_KEYS] += t[4];
+  }
+  // slide: drop the oldest level, the new tokens become the newest level
+  for (int u = lane; u < W * n1; u += 64) {
+    const int l = u / W, k = u - l * W;
+    io.win[u] = l + 1 < n1 ? win[(l + 1) * W + k] : a[1 + (n1 - 1) * W + k];
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_kv_commit(KvCommit c) {
+  const int l = blockIdx.x, j = blockIdx.y;
+  const int n = c.st->commit_n;
+  if (j >= n) return;
+  const int row = c.st->commit_rows[j];
+  const int p = c.st->commit_p + j;
+  const int nk = c.Hkv * c.hd;
+  const T* kb = (const T*)c.kb + ((size_t)l * c.M + row) * nk;
+  const T* vb = (const T*)c.vb + ((size_t)l * c.M + row) * nk;
+  T* kc = (T*)c.kc + (size_t)l * c.Hkv * c.ld_ctx * c.hd;
+  T* vc = (T*)c.vc + (size_t)l * c.Hkv * c.ld_ctx * c.hd;
+  for (int u = threadIdx.x; u < nk; u += blockDim.x) {
+    const int kvh = u / c.hd, i = u - kvh * c.hd;
+    const size_t dst = ((size_t)kvh * c.ld_ctx + p) * c.hd + i;
+    kc[dst] = kb[u];
+    vc[dst] = vb[u];
+  }
+}
+
+// Prompt as reference: insert prompt[j .. j+N-1] for j = 0 .. n-N in order.
+__global__ void k_pool_seed(PoolDesc pool, DevState* st, const int32_t* prompt, int n) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  InsertCounts c = {0, 0, 0, 0, 0};
+  for (int j = 0; j + pool.n1 < n; ++j) pool_insert(pool, prompt[j], prompt + j + 1, c);
+  st->stats[ST_INSERTS] += c.ins;
+  st->stats[ST_DUPS] += c.dup;
+  st->stats[ST_EVICT] += c.ev;
+  st->stats[ST_NGRAMS] += c.ngr;
+  st->stats[ST_KEYS] += c.keys;
+}
+
+__global__ void k_fill_i32(int32_t* p, int32_t v, size_t n) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+}  // namespace
+
+hipError_t launch_gather(const PoolDesc& pool, const StepIO& io, const RowLayout& lay,
+                         hipStream_t st) {
+  hipLaunchKernelGGL(k_gather, dim3(1), dim3(256), 0, st, pool, io, lay);
+  return hipGetLastError();
+}
+
+hipError_t launch_verify(const PoolDesc& pool, const StepIO& io, const RowLayout& lay,
+                         hipStream_t st) {
+  if (lay.M > VMAX_M) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_verify, dim3(1), dim3(64), 0, st, pool, io, lay);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_commit(const KvCommit& c, int dtype, hipStream_t st) {
+  dim3 grid(c.L, c.nmax);
+  if (dtype == LA_BF16)
+    hipLaunchKernelGGL(k_kv_commit<bf16_t>, grid, dim3(256), 0, st, c);
+  else
+    hipLaunchKernelGGL(k_kv_commit<float>, grid, dim3(256), 0, st, c);
+  return hipGetLastError();
+}
+
+hipError_t launch_pool_seed(const PoolDesc& pool, DevState* st, const int32_t* prompt, int n,
+                            hipStream_t st_) {
+  hipLaunchKernelGGL(k_pool_seed, dim3(1), dim3(64), 0, st_, pool, st, prompt, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_fill_i32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, v, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_bytes0(void* p, size_t n, hipStream_t st) {
+  // callers pass 4-byte multiples
+  return launch_fill_i32((int32_t*)p, 0, n / 4, st);
+}

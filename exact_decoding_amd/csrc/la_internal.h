@@ -1,0 +1,152 @@
+// Internal declarations shared by the HIP kernels and the engine.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "la.h"
+
+typedef uint16_t bf16_t;
+
+// ---------------------------------------------------------------------------
+// scalar storage types: fp32 or bf16 (round to nearest even on store)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float ld_f(const float* p) { return *p; }
+__device__ __forceinline__ float ld_f(const bf16_t* p) {
+  return __uint_as_float(((uint32_t)*p) << 16);
+}
+__device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);  // finite inputs only
+  return (bf16_t)(u >> 16);
+}
+__device__ __forceinline__ void st_f(float* p, float v) { *p = v; }
+__device__ __forceinline__ void st_f(bf16_t* p, float v) { *p = f2bf(v); }
+
+// ---------------------------------------------------------------------------
+// device-resident decoding state (one per session, in the workspace)
+// ---------------------------------------------------------------------------
+enum {
+  ST_INSERTS = 0, ST_DUPS, ST_EVICT, ST_GATHER_NE, ST_CAND_TOTAL, ST_STEPS, ST_TOKENS,
+  ST_NGRAMS, ST_KEYS, ST_HIST0, ST_COUNT = ST_HIST0 + LA_MAX_N + 1
+};
+
+struct DevState {
+  int32_t P;           // committed tokens in the KV cache
+  int32_t cur;         // current (last emitted, uncached) token
+  int32_t total;       // tokens emitted so far
+  int32_t done;        // 1 once max_new or EOS is reached
+  int32_t n_out;       // tokens emitted by the last step
+  int32_t out[LA_MAX_N];
+  int32_t ncand;       // candidates gathered this step
+  int32_t commit_p;    // P before the last step's commit
+  int32_t commit_n;    // rows committed by the last step
+  int32_t commit_rows[LA_MAX_N];
+  int32_t pad_[3];
+  long long stats[ST_COUNT];
+};
+
+// Static description of a step's block-row layout.
+struct RowLayout {
+  int N, W, G;   // W = G = 0 for plain autoregressive decoding
+  int M;         // 1 + (W + G) * (N - 1)
+};
+
+// ---------------------------------------------------------------------------
+// GEMM: y_part[s][m][n] = sum over split s of x[m][k] * w[n][k]
+// ---------------------------------------------------------------------------
+struct GemmSeg {
+  const void* w;  // [n][K] row-major
+  int n;          // rows of this segment
+};
+
+struct GemmDesc {
+  const void* x;  // [rows][K] row-major (rows padded to a multiple of 128 for bf16)
+  int rows;       // valid rows
+  int K;
+  int nseg;
+  GemmSeg seg[3];
+  int N;          // total columns (sum of segment rows)
+  int S;          // K splits
+  float* part;    // [S][rows_pad][N]
+  int rows_pad;   // leading row count of part
+};
+
+int gemm_splits(int N, int K, int dtype);
+hipError_t launch_gemm(const GemmDesc& g, int dtype, hipStream_t st);
+
+// epilogues of the split GEMM
+enum QkvDest { QKV_TO_BLOCK = 0, QKV_TO_CACHE = 1 };
+struct QkvEpi {
+  const float* part; int S; int rows_pad; int N;
+  int rows, H, Hkv, hd;
+  const int32_t* pos;      // absolute position of each row
+  const float2* rope;      // [max_ctx][hd/2] (cos, sin)
+  void* q;                 // [rows][H*hd]
+  void* kdst; void* vdst;  // block: [rows][Hkv*hd]; cache: [Hkv][ld_ctx][hd]
+  int dest; int ld_ctx;
+};
+hipError_t launch_qkv_epi(const QkvEpi& e, int dtype, hipStream_t st);
+hipError_t launch_resid_epi(const float* part, int S, int rows_pad, int N, int rows, float* x,
+                            hipStream_t st);
+hipError_t launch_silu_epi(const float* part, int S, int rows_pad, int F, int rows, void* act,
+                           int dtype, hipStream_t st);
+hipError_t launch_sum_epi(const float* part, int S, int rows_pad, int N, int rows, float* y,
+                          hipStream_t st);
+
+// norm / embedding / argmax
+hipError_t launch_rmsnorm(const float* x, const void* g, void* y, int rows, int d, float eps,
+                          int dtype, hipStream_t st);
+hipError_t launch_embed(const int32_t* ids, const void* emb, float* x, int rows, int d,
+                        int dtype, hipStream_t st);
+hipError_t launch_argmax(const float* logits, int rows, int V, int32_t* out, hipStream_t st);
+
+// attention
+struct AttnDesc {
+  const void* q;       // [rows][H*hd]
+  const void* kc;      // [Hkv][ld_ctx][hd]
+  const void* vc;
+  const void* kb;      // [M][Hkv*hd] block rows (step mode)
+  const void* vb;
+  void* out;           // [rows][H*hd]
+  const int32_t* pos;  // absolute position per row
+  const int32_t* Pdev; // committed length P on the device (step mode), or null
+  int P_host;          // used when Pdev is null
+  int rows, H, Hkv, hd, ld_ctx;
+  int causal_cache;    // 1: every key 0..pos(row) is in the cache (prefill)
+  RowLayout lay;
+};
+hipError_t launch_attention(const AttnDesc& a, int dtype, hipStream_t st);
+
+// lookahead bookkeeping kernels
+struct PoolDesc {
+  int32_t* tok;   // [V][cap][N-1]
+  int32_t* cnt;   // [V]
+  int32_t* head;  // [V]
+  int V, cap, n1; // n1 = N - 1
+};
+struct StepIO {
+  DevState* st;
+  int32_t* win;   // [(N-1)][W]
+  int32_t* cand;  // [G][N-1]
+  int32_t* ids;   // [M]
+  int32_t* pos;   // [M]
+  const int32_t* amax;  // [M]
+  int max_new, eos;
+};
+hipError_t launch_gather(const PoolDesc& pool, const StepIO& io, const RowLayout& lay,
+                         hipStream_t st);
+hipError_t launch_verify(const PoolDesc& pool, const StepIO& io, const RowLayout& lay,
+                         hipStream_t st);
+struct KvCommit {
+  const DevState* st;
+  const void* kb; const void* vb;  // [L][M][Hkv*hd]
+  void* kc; void* vc;              // [L][Hkv][ld_ctx][hd]
+  int L, M, Hkv, hd, ld_ctx, nmax;
+};
+hipError_t launch_kv_commit(const KvCommit& c, int dtype, hipStream_t st);
+hipError_t launch_pool_seed(const PoolDesc& pool, DevState* st, const int32_t* prompt, int n,
+                            hipStream_t st_);
+hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t st);
+hipError_t launch_fill_bytes0(void* p, size_t n, hipStream_t st);

@@ -1,0 +1,103 @@
+"""Convenience layer over the C-ABI binding: torch owns the device memory
+(weights, workspace) and the stream; every computation runs in libla.so."""
+from __future__ import annotations
+
+import numpy as np
+
+from . import binding as B
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def upload(arr: np.ndarray, device: str = "cuda"):
+    """numpy weight (float32, or uint16 bf16 bit patterns) -> torch device tensor."""
+    torch = _torch()
+    if arr.dtype == np.uint16:
+        t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32))
+    return t.to(device, non_blocking=False)
+
+
+class Model:
+    """A decoder registered with la_model_load.  `weights` are device tensors
+    (or numpy arrays, uploaded here) in loader order."""
+
+    def __init__(self, shape, weights, stream=None, device: str = "cuda"):
+        torch = _torch()
+        self.shape = shape
+        self.device = device
+        self.tensors = [w if isinstance(w, torch.Tensor) else upload(w, device) for w in weights]
+        self.stream = stream if stream is not None else torch.cuda.Stream(device=device)
+        self.dtype = B.LA_BF16 if shape.dtype == "bf16" else B.LA_F32
+        desc = B.ModelDesc(shape.n_layers, shape.d_model, shape.n_heads, shape.n_kv_heads,
+                           shape.head_dim, shape.d_ff, shape.vocab, shape.rope_theta,
+                           shape.norm_eps, self.dtype)
+        torch.cuda.synchronize(device)
+        self.handle = B.la_model_load(desc, self.tensors, self.stream)
+
+    def session(self, prompt, N: int, W: int, G: int, max_new: int, window=None,
+                prompt_ref: bool = False, ar: bool = False, graph: bool = True,
+                max_ctx: int | None = None, pool_cap: int = 0, eos_id: int = -1) -> "Session":
+        flags = (B.LA_PROMPT_REF if prompt_ref else 0) | (B.LA_AR if ar else 0)
+        flags |= 0 if graph else B.LA_NO_GRAPH
+        if max_ctx is None:
+            max_ctx = len(prompt) + max_new + N + W + 2
+        p = B.DecodeParams(N, W, G, pool_cap, max_ctx, max_new, eos_id, flags)
+        return Session(self, p, prompt, window)
+
+    def close(self):
+        if self.handle:
+            B.la_model_free(self.handle)
+            self.handle = None
+
+
+class Session:
+    def __init__(self, model: Model, params: B.DecodeParams, prompt, window):
+        torch = _torch()
+        self.model = model
+        self.params = params
+        nbytes = B.la_session_bytes(model.handle, params)
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=model.device)
+        torch.cuda.synchronize(model.device)
+        self.handle = B.la_prefill(model.handle, params, prompt, window, self.workspace,
+                                   model.stream)
+        self.rows = B.la_session_rows(self.handle)
+        self.done = False
+        self.tokens: list[int] = []
+        self.per_step: list[int] = []
+
+    def step(self) -> list[int]:
+        rc, toks = B.la_step(self.handle, max(self.params.N, 1))
+        self.tokens.extend(toks)
+        if toks:
+            self.per_step.append(len(toks))
+        self.done = rc == B.LA_DONE
+        return toks
+
+    def step_profile(self) -> tuple[list[int], dict]:
+        rc, toks, prof = B.la_step_profile(self.handle, max(self.params.N, 1))
+        self.tokens.extend(toks)
+        if toks:
+            self.per_step.append(len(toks))
+        self.done = rc == B.LA_DONE
+        return toks, prof
+
+    def decode(self) -> list[int]:
+        while not self.done:
+            self.step()
+        return self.tokens
+
+    def stats(self) -> dict:
+        return B.la_pool_stats(self.handle)
+
+    def logits(self, rows: int | None = None) -> np.ndarray:
+        return B.la_debug_logits(self.handle, rows or self.rows, self.model.shape.vocab)
+
+    def close(self):
+        if self.handle:
+            B.la_session_free(self.handle)
+            self.handle = None

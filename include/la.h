@@ -1,0 +1,208 @@
+/*
+ * la.h -- C-ABI of the lookahead decoding step on one AMD MI355X (gfx950).
+ *
+ * The calls follow the problem as stated in "Break the Sequential Dependency
+ * of LLM Inference Using LOOKAHEAD DECODING" (cited [LD]): a prompt x0
+ * (§3.4 "Mathematical Reformulation"), the hyperparameters W, N, G (§3.4
+ * "The Lookahead Branch", "N-gram selection from the pool"), one step that
+ * returns the accepted tokens -- at least one (§3.4 "Greedy verification
+ * algorithm (Algorithm 3)") -- and the observable step compression and pool
+ * (§3.4 "Scaling Law", §3.4 "N-gram pool update").
+ *
+ * Conventions for every call:
+ *  - Return value: LA_OK (0), LA_DONE (1, la_step only) or a negative
+ *    la_status.  On error, la_last_error() returns a thread-local message.
+ *    No C++ exception crosses this boundary.
+ *  - "device pointer": memory of the current HIP device (e.g. a torch
+ *    tensor's data_ptr()); "host pointer": ordinary CPU memory.
+ *  - Streams: a hipStream_t passed as void*; NULL means the null stream.
+ *    All device work of a model / session is enqueued on its stream.
+ *  - The library never frees caller memory and allocates no device memory:
+ *    all session state lives in the caller's workspace.
+ */
+#ifndef LA_H
+#define LA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LA_OK = 0,
+  LA_DONE = 1,       /* la_step: max_new tokens emitted or EOS emitted */
+  LA_EINVAL = -1,    /* bad argument (checked before any device work)   */
+  LA_ENOMEM = -2,    /* workspace too small                              */
+  LA_ECTX = -3,      /* context full: next step would pass max_ctx       */
+  LA_EHIP = -4,      /* a HIP call failed; the session is poisoned       */
+  LA_ESTATE = -5     /* call not valid in the object's state             */
+} la_status;
+
+typedef enum { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
+
+/* Upper bound on N (n-gram length). */
+#define LA_MAX_N 16
+
+/* Decoder shape (a LLaMA-shaped decoder: RMSNorm, rotate-half RoPE,
+ * SiLU-gated MLP, MHA or GQA, untied embedding and LM head).  The pages
+ * evaluate LLaMA-2 / CodeLlama ([LD] §5 "Evaluation Methodology"). */
+typedef struct {
+  int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim, d_ff, vocab;
+  float rope_theta;  /* RoPE base, e.g. 10000                         */
+  float norm_eps;    /* RMSNorm epsilon, e.g. 1e-5                     */
+  int32_t dtype;     /* la_dtype of weights, KV cache and activations */
+} la_model_desc;
+
+/* Decode parameters.
+ * N  n-gram length (2..LA_MAX_N); the window has N-1 levels ([LD] §3.4
+ *    "The Lookahead Branch").
+ * W  window width (columns), >= 0.
+ * G  max verification candidates per step, >= 0 ([LD] §3.4 "N-gram
+ *    selection from the pool").
+ * pool_cap   suffixes kept per first token (FIFO); 0 means G (min 1).
+ * max_ctx    KV-cache capacity in positions.
+ * max_new    tokens to generate.
+ * eos_id     stop after emitting this id; -1 for none.
+ * flags      LA_PROMPT_REF: seed the pool with the prompt's n-grams
+ *              ([LD] §5 Table 3, prompt as reference).
+ *            LA_AR: plain greedy autoregressive decoding through the same
+ *              kernels (W = G = 0 internally; one token per step).
+ *            LA_NO_GRAPH: launch every step's kernels eagerly instead of
+ *              replaying a captured HIP graph. */
+typedef struct {
+  int32_t N, W, G, pool_cap, max_ctx, max_new, eos_id;
+  uint32_t flags;
+} la_decode_params;
+
+#define LA_PROMPT_REF 1u
+#define LA_AR 2u
+#define LA_NO_GRAPH 8u
+
+/* Statistics since prefill ([LD] §3.4 "Scaling Law": S = tokens / steps). */
+typedef struct {
+  int64_t steps, tokens;
+  int64_t accept_hist[LA_MAX_N + 1]; /* steps that accepted j candidate tokens */
+  int64_t pool_ngrams, pool_keys_nonempty;
+  int64_t inserts, dup_skips, evictions;
+  int64_t gathers_nonempty, cand_total;
+} la_pool_stats_t;
+
+typedef struct la_model la_model;
+typedef struct la_session la_session;
+
+/* Register a model.  `dev_weights` holds n_weights = 3 + 9*n_layers device
+ * pointers, owned by the caller, in this order:
+ *   emb [vocab][d], then per layer: attn_norm [d], wq [H*hd][d],
+ *   wk [Hkv*hd][d], wv [Hkv*hd][d], wo [d][H*hd], mlp_norm [d],
+ *   wg [d_ff][d], wu [d_ff][d], wd [d][d_ff], then final_norm [d],
+ *   lm_head [vocab][d].
+ * Matrices are row-major [out][in] of the model dtype.  They must stay
+ * valid until la_model_free.  bf16 models need d, H*hd and d_ff to be
+ * multiples of 64 and H*hd, Hkv*hd multiples of 128; head_dim <= 128 and
+ * even.  *out receives a library-owned handle. */
+int la_model_load(const la_model_desc* d, const void* const* dev_weights, int n_weights,
+                  void* hip_stream, la_model** out);
+void la_model_free(la_model* m);
+
+/* Device workspace bytes a session with these parameters needs (pure host
+ * computation; no device call). */
+int la_session_bytes(const la_model* m, const la_decode_params* p, size_t* bytes);
+
+/* Prefill ([LD] §3.4: the prompt x0 is the verified prefix).
+ * prompt: host pointer, n_prompt >= 1 tokens in [0, vocab).  The first
+ *   n_prompt-1 tokens are run causally into the KV cache; the last becomes
+ *   the current token.
+ * init_window: host pointer to (N-1)*W ids, level-major (level 0 = oldest),
+ *   or NULL for all zeros.  Ignored with LA_AR.
+ * dev_workspace: device pointer of ws_bytes >= la_session_bytes(); owned by
+ *   the caller, must outlive the session, and must not be shared by two
+ *   live sessions.
+ * Host arrays are copied before return.  The call returns after the prefill
+ * has been enqueued and (unless LA_NO_GRAPH) the step graph captured; it
+ * synchronises the stream.  *out receives a library-owned session. */
+int la_prefill(la_model* m, const la_decode_params* p, const int32_t* prompt, int32_t n_prompt,
+               const int32_t* init_window, void* dev_workspace, size_t ws_bytes,
+               void* hip_stream, la_session** out);
+
+/* One lookahead decoding step: candidate gather, one forward pass over
+ * M = 1 + (W+G)(N-1) rows under the lookahead mask ([LD] §3.4 "The custom
+ * attention mask (Figure 2)"), greedy verification (Algorithm 3), KV
+ * commit, window slide and pool insert.  Blocks until the emitted tokens
+ * are on the host.
+ * out_tokens: host pointer with room for out_cap >= N ids.
+ * *n_out: tokens written (1..N while decoding; fewer on the last step).
+ * Returns LA_OK, LA_DONE (budget or EOS reached by this or an earlier
+ * step; *n_out may be > 0), LA_ECTX (no device work done), or an error. */
+int la_step(la_session* s, int32_t* out_tokens, int32_t out_cap, int32_t* n_out);
+
+/* Per-kernel-class timing of one step (benchmark hook). */
+enum {
+  LA_PROF_GEMM = 0,   /* QKV, O, gate/up, down projections            */
+  LA_PROF_LMHEAD,     /* LM-head GEMM                                 */
+  LA_PROF_ATTN,       /* lookahead attention                          */
+  LA_PROF_NORM,       /* RMSNorm, embedding                           */
+  LA_PROF_EPI,        /* split-K reduce / RoPE / SiLU / residual      */
+  LA_PROF_ARGMAX,     /* per-row argmax                               */
+  LA_PROF_BOOK,       /* gather, verify + window + pool, KV commit    */
+  LA_PROF_KINDS
+};
+typedef struct {
+  int32_t launches[LA_PROF_KINDS];
+  double ms[LA_PROF_KINDS];     /* summed hipEvent intervals              */
+  double bytes[LA_PROF_KINDS];  /* algorithmic HBM bytes of those launches */
+  double flops[LA_PROF_KINDS];  /* algorithmic FLOPs of those launches     */
+} la_profile_t;
+
+/* la_step with every kernel launched eagerly and bracketed by a pair of
+ * hipEvents on the session's stream; *prof receives the per-class sums.
+ * Same kernels, grids and arguments as the graph replay.  Algorithmic bytes:
+ * GEMM = weights + input rows + fp32 output rows; attention = committed K/V
+ * read once per KV head + block K/V + q + output. */
+int la_step_profile(la_session* s, int32_t* out_tokens, int32_t out_cap, int32_t* n_out,
+                    la_profile_t* prof);
+
+/* Counters since prefill; synchronises the session's stream. */
+int la_pool_stats(const la_session* s, la_pool_stats_t* out);
+
+/* fp32 logits of the last step's M rows (rows <= M), row-major [rows][vocab],
+ * copied to the host pointer `out`.  Test hook. */
+int la_debug_logits(const la_session* s, float* out, int32_t rows);
+
+/* Rows in one step (M) of this session. */
+int la_session_rows(const la_session* s, int32_t* rows);
+
+void la_session_free(la_session* s);
+
+const char* la_last_error(void);
+
+/* The step's attention on its own (test / benchmark hook), for one layer:
+ * every block row q attends to the committed prefix [0, P) and to the block
+ * rows the lookahead mask lets it see.
+ *   q       [M][H*hd]          device, dtype
+ *   k_cache, v_cache [Hkv][ld_ctx][hd]  device, dtype; positions [0, P) used
+ *   k_blk, v_blk     [M][Hkv*hd]        device, dtype
+ *   out     [M][H*hd]          device, dtype (written)
+ * with M = 1 + (W+G)(N-1).  Row positions are P + offset (row layout of
+ * la_step).  Enqueued on `hip_stream`; does not synchronise. */
+int la_kernel_attention(const void* q, const void* k_cache, const void* v_cache, int32_t P,
+                        int32_t ld_ctx, const void* k_blk, const void* v_blk, void* out,
+                        int32_t H, int32_t Hkv, int32_t hd, int32_t N, int32_t W, int32_t G,
+                        int32_t dtype, void* hip_stream);
+
+/* The projection GEMM on its own (test / benchmark hook):
+ * y[m][n] = sum_k x[m][k] * w[n][k] in fp32, with the same split and
+ * summation order the step uses for an N x K weight.
+ *   x [M][K], w [N][K] device, dtype; y [M][N] device fp32 (written);
+ *   ws device scratch of ws_bytes >= la_kernel_gemm_ws_bytes(M, K, N).
+ * M >= 1; K a multiple of 64 for bf16.  Enqueued on `hip_stream`. */
+int la_kernel_gemm(const void* x, int32_t M, int32_t K, const void* w, int32_t N, float* y,
+                   int32_t dtype, void* ws, size_t ws_bytes, void* hip_stream);
+size_t la_kernel_gemm_ws_bytes(int32_t M, int32_t K, int32_t N);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LA_H */

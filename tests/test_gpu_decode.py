@@ -1,0 +1,123 @@
+"""End-to-end GPU parity of the lookahead step through the C-ABI.
+
+1. tiny fp32 model: GPU lookahead tokens == oracle greedy AR tokens; the
+   per-step accepted counts, S and pool counters equal the oracle's
+   lookahead run; the block-row logits of a step match the oracle's within
+   1e-4.
+2. bf16 models (MHA and GQA, head_dim 128): GPU lookahead tokens are
+   bit-identical to the GPU's own AR decode; GPU logits along the stream
+   match the oracle's teacher-forced logits within 2e-2; every token whose
+   oracle top-2 margin exceeds 2 * tol equals the oracle's argmax.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import synth
+from exact_decoding_amd.runtime import Model
+from oracle import lookahead as la
+from oracle.model import OracleModel
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    s = synth.SHAPES["tiny"]
+    w = synth.gen_weights(s, 0)
+    return s, w, Model(s, w), OracleModel(s, w)
+
+
+@pytest.mark.parametrize("prompt_ref", [False, True])
+@pytest.mark.parametrize("graph", [True, False])
+def test_tiny_fp32_matches_oracle(tiny, prompt_ref, graph):
+    s, w, gm, om = tiny
+    N, W, G, n_new = 3, 4, 4, 32
+    prompt = synth.prompt_motif(s.vocab, seed=1)
+    win = synth.gen_window(N, W, s.vocab, seed=2)
+    print(f"tiny fp32 prompt_ref={prompt_ref} graph={graph}", flush=True)
+    ar = la.greedy_ar(om, prompt, n_new)
+    ref = la.lookahead(om, prompt, N, W, G, n_new, win, prompt_ref=prompt_ref, keep_logits=True)
+    assert ref.tokens == ar.tokens
+    ses = gm.session(prompt, N, W, G, n_new, window=win, prompt_ref=prompt_ref, graph=graph)
+    first = ses.step()
+    lg = ses.logits()
+    np.testing.assert_allclose(lg, ref.step_logits[0], atol=1e-4, rtol=0)
+    toks = first + [t for t in ses.decode()[len(first):]]
+    assert ses.tokens == ar.tokens
+    assert ses.per_step == ref.emitted
+    st = ses.stats()
+    assert st["steps"] == ref.steps and st["tokens"] == n_new
+    assert [st["accept_hist"][j] for j in range(N)] == [ref.accepted.count(j) for j in range(N)]
+    assert st["inserts"] == ref.pool.inserts and st["dup_skips"] == ref.pool.dup_skips
+    assert st["evictions"] == ref.pool.evictions
+    assert st["pool_ngrams"] == ref.pool.n_ngrams() and st["pool_keys_nonempty"] == ref.pool.n_keys()
+    ses.close()
+    del toks
+
+
+def test_tiny_fp32_ar_session(tiny):
+    s, w, gm, om = tiny
+    prompt = synth.prompt_motif(s.vocab, seed=3)
+    ar = la.greedy_ar(om, prompt, 20)
+    ses = gm.session(prompt, 3, 4, 4, 20, ar=True)
+    assert ses.rows == 1
+    assert ses.decode() == ar.tokens
+    assert ses.per_step == [1] * 20
+    ses.close()
+
+
+def test_tiny_budget_and_eos(tiny):
+    s, w, gm, om = tiny
+    prompt = synth.prompt_motif(s.vocab, seed=1)
+    ar = la.greedy_ar(om, prompt, 30)
+    win = synth.gen_window(4, 3, s.vocab, seed=2)
+    ses = gm.session(prompt, 4, 3, 3, 7, window=win, prompt_ref=True)
+    assert ses.decode() == ar.tokens[:7]
+    ses.close()
+    eos = ar.tokens[9]
+    ses = gm.session(prompt, 4, 3, 3, 30, window=win, prompt_ref=True, eos_id=eos)
+    assert ses.decode() == ar.tokens[:ar.tokens.index(eos) + 1]
+    ses.close()
+
+
+def _bf16_case(name, N, W, G, n_new, prompt):
+    s = synth.SHAPES[name]
+    w = synth.gen_weights(s, 0)
+    gm = Model(s, w)
+    win = synth.gen_window(N, W, s.vocab, seed=2)
+    la_ses = gm.session(prompt, N, W, G, n_new, window=win, prompt_ref=True)
+    la_toks = la_ses.decode()
+    st = la_ses.stats()
+    la_ses.close()
+    ar_ses = gm.session(prompt, N, W, G, n_new, ar=True)
+    ar_logits = []
+    while not ar_ses.done:
+        ar_ses.step()
+        ar_logits.append(ar_ses.logits(1)[0])
+    ar_toks = ar_ses.tokens
+    ar_ses.close()
+    return s, w, gm, la_toks, ar_toks, np.array(ar_logits), st
+
+
+@pytest.mark.parametrize("name,N,W,G", [("small_bf16", 5, 7, 7), ("small_gqa_bf16", 4, 5, 3)])
+def test_bf16_lookahead_bit_exact_and_oracle(name, N, W, G):
+    print(f"bf16 decode {name} N={N} W={W} G={G}", flush=True)
+    s = synth.SHAPES[name]
+    prompt = synth.prompt_zipf_spans(s.vocab, length=64, seed=1)
+    n_new = 48
+    s, w, gm, la_toks, ar_toks, ar_logits, st = _bf16_case(name, N, W, G, n_new, prompt)
+    assert la_toks == ar_toks, "lookahead stream differs from the same engine's AR stream"
+    assert st["tokens"] == n_new and 1 <= n_new / st["steps"] <= N
+    om = OracleModel(s, w)
+    seq = np.concatenate([prompt, np.array(ar_toks[:-1], dtype=np.int64)])
+    ref = la.score(om, seq)[len(prompt) - 1:]
+    tol = 2e-2
+    assert np.abs(ar_logits - ref).max() < tol
+    srt = np.sort(ref, axis=1)
+    margin = srt[:, -1] - srt[:, -2]
+    top = np.argmax(ref, axis=1)
+    sure = margin > 2 * tol
+    assert np.array_equal(np.array(ar_toks)[sure], top[sure])
+    gm.close()

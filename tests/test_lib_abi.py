@@ -1,0 +1,109 @@
+"""Host-side checks of the C-ABI library (no GPU needed): it loads, exports
+every call include/la.h declares, and rejects bad arguments before any
+device work."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from exact_decoding_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "la.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(la_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    lib = B.load_library()
+    names = _declared()
+    assert "la_step" in names and "la_prefill" in names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(B.EXPORTS) == set(names)
+
+
+def _model(dtype=B.LA_BF16, L=2, d=512, H=4, Hkv=4, hd=128, F=1408, V=4000):
+    desc = B.ModelDesc(L, d, H, Hkv, hd, F, V, 10000.0, 1e-5, dtype)
+    # la_model_load only records the pointers: fake non-null values are fine
+    fake = [ctypes.c_void_p(0x1000 + 256 * i) for i in range(3 + 9 * L)]
+    arr = (ctypes.c_void_p * len(fake))(*fake)
+    lib = B.load_library()
+    out = ctypes.c_void_p()
+    rc = lib.la_model_load(ctypes.byref(desc), arr, len(fake), None, ctypes.byref(out))
+    return rc, out
+
+
+def test_model_load_validation():
+    rc, m = _model()
+    assert rc == B.LA_OK and m.value
+    B.la_model_free(m)
+    assert _model(hd=96)[0] == B.LA_EINVAL
+    assert _model(H=4, Hkv=3)[0] == B.LA_EINVAL
+    assert _model(d=500)[0] == B.LA_EINVAL          # bf16 needs d % 64 == 0
+    assert _model(dtype=B.LA_F32, d=500, H=4, hd=16, F=100)[0] == B.LA_OK
+    assert _model(dtype=7)[0] == B.LA_EINVAL
+
+
+def test_session_bytes_and_param_validation():
+    rc, m = _model()
+    p = B.DecodeParams(5, 15, 15, 0, 400, 256, -1, B.LA_PROMPT_REF)
+    n = B.la_session_bytes(m, p)
+    assert n > 0
+    p_ar = B.DecodeParams(5, 15, 15, 0, 400, 256, -1, B.LA_AR)
+    assert 0 < B.la_session_bytes(m, p_ar) < n
+    for bad in [B.DecodeParams(1, 4, 4, 0, 100, 10, -1, 0), B.DecodeParams(17, 4, 4, 0, 100, 10, -1, 0),
+                B.DecodeParams(3, -1, 4, 0, 100, 10, -1, 0), B.DecodeParams(3, 4, 4, 0, 100, 0, -1, 0),
+                B.DecodeParams(3, 4, 4, 0, 100, 10, 4000, 0), B.DecodeParams(3, 4, 4, 0, 100, 10, -1, 64),
+                B.DecodeParams(16, 100, 100, 0, 100, 10, -1, 0)]:
+        with pytest.raises(B.LaError) as e:
+            B.la_session_bytes(m, bad)
+        assert e.value.code == B.LA_EINVAL
+    B.la_model_free(m)
+
+
+def test_prefill_rejects_before_device_work():
+    lib = B.load_library()
+    rc, m = _model()
+    p = B.DecodeParams(3, 4, 4, 0, 64, 8, -1, B.LA_NO_GRAPH)
+    prompt = (ctypes.c_int32 * 4)(1, 2, 3, 4)
+    out = ctypes.c_void_p()
+    ws = ctypes.c_void_p(0x10000)
+    # workspace too small
+    assert lib.la_prefill(m, ctypes.byref(p), prompt, 4, None, ws, 16, None, ctypes.byref(out)) == B.LA_ENOMEM
+    need = B.la_session_bytes(m, p)
+    # token out of range
+    bad = (ctypes.c_int32 * 4)(1, 2, 3, 4000)
+    assert lib.la_prefill(m, ctypes.byref(p), bad, 4, None, ws, need, None, ctypes.byref(out)) == B.LA_EINVAL
+    # empty prompt
+    assert lib.la_prefill(m, ctypes.byref(p), prompt, 0, None, ws, need, None, ctypes.byref(out)) == B.LA_EINVAL
+    # prompt too long for max_ctx
+    long_prompt = (ctypes.c_int32 * 70)(*([1] * 70))
+    assert lib.la_prefill(m, ctypes.byref(p), long_prompt, 70, None, ws, need, None, ctypes.byref(out)) == B.LA_ECTX
+    # graph mode needs a stream
+    p2 = B.DecodeParams(3, 4, 4, 0, 64, 8, -1, 0)
+    assert lib.la_prefill(m, ctypes.byref(p2), prompt, 4, None, ws, need, None, ctypes.byref(out)) == B.LA_EINVAL
+    assert b"stream" in lib.la_last_error()
+    B.la_model_free(m)
+
+
+def test_step_null_args():
+    lib = B.load_library()
+    n = ctypes.c_int32()
+    assert lib.la_step(None, None, 4, ctypes.byref(n)) == B.LA_EINVAL
+
+
+def test_kernel_hooks_validate():
+    lib = B.load_library()
+    P = ctypes.c_void_p(0x1000)
+    # bad head_dim / N
+    assert lib.la_kernel_attention(P, P, P, 4, 8, P, P, P, 4, 4, 100, 3, 2, 2, 1, None) == B.LA_EINVAL
+    assert lib.la_kernel_attention(P, P, P, 4, 8, P, P, P, 4, 4, 128, 1, 2, 2, 1, None) == B.LA_EINVAL
+    assert lib.la_kernel_attention(P, P, P, 9, 8, P, P, P, 4, 4, 128, 3, 2, 2, 1, None) == B.LA_EINVAL
+    # bf16 GEMM needs K % 64 == 0
+    assert lib.la_kernel_gemm(P, 4, 100, P, 64, P, B.LA_BF16, None, 0, None) == B.LA_EINVAL
+    assert B.la_kernel_gemm_ws_bytes(121, 4096, 4096) > 0
