@@ -158,7 +158,8 @@ def main():
     la_tokens_ref = list(ses.tokens)
     ses.close()
     S = args.max_new / gen_steps
-    log(f"[bench] one generation: {gen_steps} steps, S = {S:.3f}")
+    log(f"[bench] one generation: {gen_steps} steps, S = {S:.3f}; {len(set(la_tokens_ref))} distinct "
+        f"tokens; first 48: {la_tokens_ref[:48]}; last 24: {la_tokens_ref[-24:]}")
 
     n_sess = math.ceil(args.steps / gen_steps) + 1
     log(f"[bench] timing {args.steps} lookahead steps over {n_sess} pre-filled sessions")

@@ -24,6 +24,7 @@ EXPORTS = [
     "la_model_load", "la_model_free", "la_session_bytes", "la_prefill", "la_step",
     "la_pool_stats", "la_debug_logits", "la_session_rows", "la_session_free", "la_last_error",
     "la_kernel_attention", "la_kernel_gemm", "la_kernel_gemm_ws_bytes", "la_step_profile",
+    "la_kernel_attention_ws_bytes", "la_packed_bytes", "la_pack_weight", "la_probe_read",
 ]
 
 PROF_KINDS = ["gemm", "lm_head", "attention", "norm", "epilogue", "argmax", "bookkeeping"]
@@ -103,8 +104,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.la_last_error.argtypes = []
     lib.la_last_error.restype = ctypes.c_char_p
     lib.la_kernel_attention.argtypes = [P, P, P, I32, I32, P, P, P, I32, I32, I32, I32, I32, I32,
-                                        I32, P]
+                                        I32, P, SZ, P]
+    lib.la_kernel_attention_ws_bytes.argtypes = [I32, I32, I32, I32, I32, I32, I32]
+    lib.la_kernel_attention_ws_bytes.restype = SZ
     lib.la_kernel_gemm.argtypes = [P, I32, I32, P, I32, P, I32, P, SZ, P]
+    lib.la_probe_read.argtypes = [P, SZ, P, P]
+    lib.la_packed_bytes.argtypes = [I32, I32]
+    lib.la_packed_bytes.restype = SZ
+    lib.la_pack_weight.argtypes = [P, I32, I32, P, P]
     lib.la_kernel_gemm_ws_bytes.argtypes = [I32, I32, I32]
     lib.la_kernel_gemm_ws_bytes.restype = SZ
     _lib = lib
@@ -204,12 +211,31 @@ def la_model_free(model) -> None:
     load_library().la_model_free(model)
 
 
+def la_kernel_attention_ws_bytes(ld_ctx, H, hd, N, W, G, dtype) -> int:
+    return int(load_library().la_kernel_attention_ws_bytes(ld_ctx, H, hd, N, W, G, dtype))
+
+
 def la_kernel_attention(q, k_cache, v_cache, P, ld_ctx, k_blk, v_blk, out, H, Hkv, hd, N, W, G,
-                        dtype, stream) -> None:
+                        dtype, ws, stream) -> None:
     lib = load_library()
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib.la_kernel_attention(_ptr(q), _ptr(k_cache), _ptr(v_cache), P, ld_ctx, _ptr(k_blk),
-                                   _ptr(v_blk), _ptr(out), H, Hkv, hd, N, W, G, dtype,
-                                   ctypes.c_void_p(_stream_handle(stream))))
+                                   _ptr(v_blk), _ptr(out), H, Hkv, hd, N, W, G, dtype, _ptr(ws),
+                                   nbytes, ctypes.c_void_p(_stream_handle(stream))))
+
+
+def la_probe_read(buf, nbytes: int, out, stream) -> None:
+    _check(load_library().la_probe_read(_ptr(buf), nbytes, _ptr(out),
+                                        ctypes.c_void_p(_stream_handle(stream))))
+
+
+def la_packed_bytes(N: int, K: int) -> int:
+    return int(load_library().la_packed_bytes(N, K))
+
+
+def la_pack_weight(src, N: int, K: int, dst, stream) -> None:
+    _check(load_library().la_pack_weight(_ptr(src), N, K, _ptr(dst),
+                                         ctypes.c_void_p(_stream_handle(stream))))
 
 
 def la_kernel_gemm_ws_bytes(M: int, K: int, N: int) -> int:

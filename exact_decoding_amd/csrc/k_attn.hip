@@ -14,7 +14,16 @@
 // that step.
 #include "la_internal.h"
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
 namespace {
+
+union U4 {
+  uint4 u;
+  bf16x8_t v;
+  bf16_t h[8];
+};
 
 // Block row holding the key at position P + j for block row `r` (0 <= j <=
 // pos(r) - P).
@@ -57,48 +66,75 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// dot(q, k) over HD in order d = 0..HD-1 (16-byte loads of k)
+// dot(q, k) over HD: four interleaved partial sums (dimension d goes to
+// partial d mod 4, each partial in increasing d), added as (p0+p1)+(p2+p3).
 template <int HD>
 __device__ __forceinline__ float dot_q(const float* qs, const bf16_t* k) {
-  float acc = 0.f;
+  float a[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int d0 = 0; d0 < HD; d0 += 8) {
     const uint4 u = *(const uint4*)(k + d0);
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      acc = fmaf(qs[d0 + 2 * e], __uint_as_float(w[e] << 16), acc);
-      acc = fmaf(qs[d0 + 2 * e + 1], __uint_as_float(w[e] & 0xFFFF0000u), acc);
+      a[(2 * e) & 3] = fmaf(qs[d0 + 2 * e], __uint_as_float(w[e] << 16), a[(2 * e) & 3]);
+      a[(2 * e + 1) & 3] =
+          fmaf(qs[d0 + 2 * e + 1], __uint_as_float(w[e] & 0xFFFF0000u), a[(2 * e + 1) & 3]);
     }
   }
-  return acc;
+  return (a[0] + a[1]) + (a[2] + a[3]);
 }
 template <int HD>
 __device__ __forceinline__ float dot_q(const float* qs, const float* k) {
-  float acc = 0.f;
+  float a[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int d0 = 0; d0 < HD; d0 += 4) {
     const float4 u = *(const float4*)(k + d0);
-    acc = fmaf(qs[d0], u.x, acc);
-    acc = fmaf(qs[d0 + 1], u.y, acc);
-    acc = fmaf(qs[d0 + 2], u.z, acc);
-    acc = fmaf(qs[d0 + 3], u.w, acc);
+    a[0] = fmaf(qs[d0], u.x, a[0]);
+    a[1] = fmaf(qs[d0 + 1], u.y, a[1]);
+    a[2] = fmaf(qs[d0 + 2], u.z, a[2]);
+    a[3] = fmaf(qs[d0 + 3], u.w, a[3]);
   }
-  return acc;
+  return (a[0] + a[1]) + (a[2] + a[3]);
 }
 
-// One wave per (head, row).  Lane j of a tile scores the key at position
-// 64t + j; lanes own output dimensions lane, lane+64 for the P.V sum.
+constexpr int AT = 64;  // attention tile (positions)
+
+// End of the MFMA part of a row's keys (a multiple of AT): at least D keys
+// before the row's own position stay in the per-row part, and never a block
+// position (>= P).  A verification row at P+i (i <= D) and the
+// autoregressive query at the same position get the same split.
+__device__ __forceinline__ int bulk_end(int pos, int P, int D) {
+  int f = pos - D;
+  f = f < 0 ? 0 : (f / AT) * AT;
+  const int pf = (P / AT) * AT;
+  return f < pf ? f : pf;
+}
+
+__device__ __forceinline__ int row_pos(const AttnDesc& a, int r, int Pc) {
+  return a.pos ? a.pos[r] : Pc + row_offset(r, a.lay);
+}
+
+// Per-row part: one wave per (head, row) over positions [F, pos] in
+// absolute-position tiles of 64 (keys from the cache below P, from the
+// block chain above).  Lane j of a tile scores the key at position 64t + j;
+// lanes own output dimensions lane, lane+64 for the P.V sum.  Writes the
+// normalised output when there is no MFMA part, else (m, l, o) partials.
 template <typename T, int HD>
-__global__ __launch_bounds__(64) void k_attn(AttnDesc a) {
-  constexpr int NPL = (HD + 63) / 64;  // output dims per lane
+__global__ __launch_bounds__(64) void k_attn_tail(AttnDesc a) {
+  // keys per pass: two per lane when the staged V rows fit in LDS
+  constexpr int KP = (int)sizeof(T) * HD <= 256 ? 128 : 64;
+  constexpr int DPL = HD >= 64 ? HD / 64 : 1;        // output dims per lane (contiguous)
+  constexpr int VSTRIDE = HD + 16 / (int)sizeof(T);  // padded LDS row of V
   __shared__ float qs[HD];
-  __shared__ float ps[64];
+  __shared__ float ps[KP];
+  __shared__ __align__(16) T vs[KP * VSTRIDE];
   const int h = blockIdx.x, r = blockIdx.y, lane = threadIdx.x;
   const int kvh = h * a.Hkv / a.H;
   const int Pc = a.Pdev ? *a.Pdev : a.P_host;
-  const int pos = a.pos ? a.pos[r] : Pc + row_offset(r, a.lay);
+  const int pos = row_pos(a, r, Pc);
   const int P = a.causal_cache ? pos + 1 : Pc;
+  const int F = a.chunk > 0 ? bulk_end(pos, P, a.D) : 0;
   const int ldb = a.Hkv * HD;
   const T* q = (const T*)a.q + (size_t)r * a.H * HD + h * HD;
   const T* kc = (const T*)a.kc + (size_t)kvh * a.ld_ctx * HD;
@@ -108,50 +144,293 @@ __global__ __launch_bounds__(64) void k_attn(AttnDesc a) {
   for (int i = lane; i < HD; i += 64) qs[i] = ld_f(q + i);
   __syncthreads();
   const float scale = 1.0f / sqrtf((float)HD);
+  const int d0 = lane * DPL;
+  const bool down = d0 < HD;
 
   float m_run = -INFINITY, l_run = 0.f;
-  float o[NPL];
+  float o[DPL];
 #pragma unroll
-  for (int j = 0; j < NPL; ++j) o[j] = 0.f;
+  for (int j = 0; j < DPL; ++j) o[j] = 0.f;
 
-  const int ntiles = pos / 64 + 1;
-  for (int t = 0; t < ntiles; ++t) {
-    const int p = t * 64 + lane;
-    float s = -INFINITY;
-    if (p <= pos) {
-      const T* kp = p < P ? kc + (size_t)p * HD
-                          : kb + (size_t)chain_row(r, p - P, a.lay) * ldb;
-      s = dot_q<HD>(qs, kp) * scale;
+  // passes over [F, pos] aligned to multiples of KP in absolute position
+  for (int base = (F / KP) * KP; base <= pos; base += KP) {
+    const int lo = base > F ? base : F;
+    const int hi = min(pos, base + KP - 1);
+    float sc[KP / 64];
+#pragma unroll
+    for (int u = 0; u < KP / 64; ++u) {
+      const int p = base + u * 64 + lane;
+      sc[u] = -INFINITY;
+      if (p >= lo && p <= hi) {
+        const int src = p < P ? -1 : chain_row(r, p - P, a.lay);
+        const T* kp = src < 0 ? kc + (size_t)p * HD : kb + (size_t)src * ldb;
+        const T* vp = src < 0 ? vc + (size_t)p * HD : vb + (size_t)src * ldb;
+#pragma unroll
+        for (int e = 0; e < HD * (int)sizeof(T) / 16; ++e)
+          *(uint4*)((char*)(vs + (u * 64 + lane) * VSTRIDE) + 16 * e) = *((const uint4*)vp + e);
+        sc[u] = dot_q<HD>(qs, kp) * scale;
+      }
     }
-    const float m_new = fmaxf(m_run, wave_max(s));
-    const float alpha = expf(m_run - m_new);
-    const float pj = p <= pos ? expf(s - m_new) : 0.f;
-    l_run = l_run * alpha + wave_sum(pj);
-    m_run = m_new;
-    ps[lane] = pj;
+    float mp = sc[0];
+#pragma unroll
+    for (int u = 1; u < KP / 64; ++u) mp = fmaxf(mp, sc[u]);
+    mp = wave_max(mp);
+    float lp = 0.f;
+#pragma unroll
+    for (int u = 0; u < KP / 64; ++u) {
+      const float pv = sc[u] == -INFINITY ? 0.f : expf(sc[u] - mp);
+      ps[u * 64 + lane] = pv;
+      lp += pv;
+    }
+    lp = wave_sum(lp);
+    __syncthreads();
+    // P.V over this pass: key j goes to partial j mod 4
+    float acc[4][DPL];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) acc[t][j] = 0.f;
+    if (down) {
+      const int n = hi - base + 1;
+      for (int jj = lo - base; jj < n; jj += 4) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          if (jj + t < n) {
+            const float w = ps[jj + t];
+            const T* vr = vs + (jj + t) * VSTRIDE + d0;
+#pragma unroll
+            for (int j = 0; j < DPL; ++j) acc[t][j] = fmaf(w, ld_f(vr + j), acc[t][j]);
+          }
+        }
+      }
+    }
+    // fold the pass into the running state
+    const float mn = fmaxf(m_run, mp);
+    const float ca = m_run == -INFINITY ? 0.f : expf(m_run - mn);
+    const float cb = expf(mp - mn);
+    l_run = l_run * ca + lp * cb;
+#pragma unroll
+    for (int j = 0; j < DPL; ++j)
+      o[j] = o[j] * ca + ((acc[0][j] + acc[1][j]) + (acc[2][j] + acc[3][j])) * cb;
+    m_run = mn;
+    __syncthreads();
+  }
+
+  // merge: the MFMA chunks of [0, F) in chunk order, then this row's part
+  float m = -INFINITY, l = 0.f, oo[DPL];
+#pragma unroll
+  for (int j = 0; j < DPL; ++j) oo[j] = 0.f;
+  for (int sp = 0; a.chunk > 0 && sp * a.chunk < F; ++sp) {
+    const size_t pb = ((size_t)sp * a.rows + r) * a.H + h;
+    const float ms = a.part_ml[pb * 2], lsum = a.part_ml[pb * 2 + 1];
+    const float mn = fmaxf(m, ms);
+    const float ca = m == -INFINITY ? 0.f : expf(m - mn);
+    const float cb = expf(ms - mn);
+    l = l * ca + lsum * cb;
+    if (down)
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) oo[j] = oo[j] * ca + a.part_o[pb * HD + d0 + j] * cb;
+    m = mn;
+  }
+  {
+    const float mn = fmaxf(m, m_run);
+    const float ca = m == -INFINITY ? 0.f : expf(m - mn);
+    const float cb = expf(m_run - mn);
+    l = l * ca + l_run * cb;
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) oo[j] = oo[j] * ca + o[j] * cb;
+  }
+  T* out = (T*)a.out + (size_t)r * a.H * HD + h * HD;
+  const float inv = 1.0f / l;
+  if (down)
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) st_f(out + d0 + j, oo[j] * inv);
+}
+
+// MFMA part (bf16, head_dim 128): one workgroup per (head, chunk of `chunk`
+// committed positions, block of 128 rows).  Each 64-position tile of K and V
+// is staged in LDS once and used by every row; wave w handles the 16-row
+// groups w and w+4.
+//
+// Scores are computed transposed, S^T = K Q^T (v_mfma_f32_16x16x32_bf16,
+// A = 16 keys x 32 dims of K, B = 32 dims x 16 rows of Q^T), so a lane holds
+// 16 scores of one row (row = lane % 16, keys 16kb + 4(lane/16) + e); the
+// row's softmax statistics then need a reduction over 4 lanes only, and the
+// probabilities are already in the A-operand layout of P.V: for the 32-key
+// step j, MFMA slot (lane/16, s) carries key 32j + 4(lane/16) + s (s < 4) or
+// 32j + 16 + 4(lane/16) + s - 4, and V is read transposed from LDS with the
+// same key order.  A tile that lies past a row's bulk end leaves that row's
+// state unchanged (alpha = 1, p = 0).
+constexpr int KSTR = 128 + 8;  // LDS row stride of K (bf16)
+constexpr int VSTR = AT + 8;   // LDS row stride of V^T (bf16)
+
+__global__ __launch_bounds__(256) void k_attn_bulk(AttnDesc a) {
+  __shared__ __align__(16) bf16_t Ks[AT * KSTR];
+  __shared__ __align__(16) bf16_t Vt[128 * VSTR];
+  const int h = blockIdx.x, split = blockIdx.y, rb = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c16 = lane & 15, q4 = lane >> 4;
+  const int kvh = h * a.Hkv / a.H;
+  const int Pc = a.Pdev ? *a.Pdev : a.P_host;
+  const int row0 = rb * 128;
+  const int nrows = min(128, a.rows - row0);
+  const int ngroups = (nrows + 15) >> 4;
+  const int s0 = split * a.chunk;
+  const bf16_t* kc = (const bf16_t*)a.kc + (size_t)kvh * a.ld_ctx * 128;
+  const bf16_t* vc = (const bf16_t*)a.vc + (size_t)kvh * a.ld_ctx * 128;
+  const float scale = 1.0f / sqrtf(128.0f);
+
+  // this wave's row groups; per lane: row = group*16 + c16
+  int F[2];
+  bool gon[2];
+  U4 qf[2][4];
+  f32x4_t o[2][8];
+  float m_run[2], l_run[2];
+  int tend = 0;  // tiles below this may be valid for some row of the workgroup
+#pragma unroll
+  for (int gi = 0; gi < 2; ++gi) {
+    const int g = wave + 4 * gi;
+    gon[gi] = g < ngroups;
+    const int rl = g * 16 + c16;
+    const int r = row0 + rl;
+    F[gi] = 0;
+    if (gon[gi] && rl < nrows) {
+      const int pos = row_pos(a, r, Pc);
+      const int P = a.causal_cache ? pos + 1 : Pc;
+      F[gi] = bulk_end(pos, P, a.D);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (gon[gi] && rl < nrows)
+        qf[gi][ks].u = *(const uint4*)((const bf16_t*)a.q + (size_t)r * a.H * 128 + h * 128 +
+                                       ks * 32 + q4 * 8);
+      else
+        qf[gi][ks].u = make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int db = 0; db < 8; ++db) o[gi][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m_run[gi] = -INFINITY;
+    l_run[gi] = 0.f;
+  }
+  // the workgroup's furthest bulk end bounds the tile loop
+  __shared__ int s_fmax;
+  if (tid == 0) s_fmax = 0;
+  __syncthreads();
+  atomicMax(&s_fmax, max(F[0], F[1]));
+  __syncthreads();
+  tend = min(s0 + a.chunk, s_fmax);
+
+  for (int t0 = s0; t0 < tend; t0 += AT) {
+    // stage K [key][dim] and V^T [dim][key] for positions t0 .. t0+63
+    {
+      const int key = tid >> 2, seg = tid & 3;  // 32 dims per thread
+      const uint4* src = (const uint4*)(kc + (size_t)(t0 + key) * 128 + seg * 32);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *(uint4*)(&Ks[key * KSTR + seg * 32 + j * 8]) = src[j];
+      const int kp = tid & 31, vs = tid >> 5;  // key pair, 16-dim segment
+      const uint4* v0 = (const uint4*)(vc + (size_t)(t0 + 2 * kp) * 128 + vs * 16);
+      const uint4* v1 = (const uint4*)(vc + (size_t)(t0 + 2 * kp + 1) * 128 + vs * 16);
+      U4 a0, a1, b0, b1;
+      a0.u = v0[0]; a1.u = v0[1]; b0.u = v1[0]; b1.u = v1[1];
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        *(uint32_t*)(&Vt[(vs * 16 + d) * VSTR + 2 * kp]) =
+            (uint32_t)a0.h[d] | ((uint32_t)b0.h[d] << 16);
+        *(uint32_t*)(&Vt[(vs * 16 + 8 + d) * VSTR + 2 * kp]) =
+            (uint32_t)a1.h[d] | ((uint32_t)b1.h[d] << 16);
+      }
+    }
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < NPL; ++j) o[j] *= alpha;
-    const int jmax = min(63, pos - t * 64);
-    for (int jj = 0; jj <= jmax; ++jj) {
-      const int pp = t * 64 + jj;
-      const T* vp = pp < P ? vc + (size_t)pp * HD
-                           : vb + (size_t)chain_row(r, pp - P, a.lay) * ldb;
-      const float w = ps[jj];
+    for (int gi = 0; gi < 2; ++gi) {
+      if (!gon[gi]) continue;
+      const bool valid = t0 + AT <= F[gi];
+      // skip the group when the tile is past every one of its rows
+      const bool any = __any(valid);
+      if (!any) continue;
+      f32x4_t st[4];
 #pragma unroll
-      for (int j = 0; j < NPL; ++j) {
-        const int d = lane + 64 * j;
-        if (d < HD) o[j] = fmaf(w, ld_f(vp + d), o[j]);
+      for (int kb = 0; kb < 4; ++kb) {
+        st[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          U4 ka;
+          ka.u = *(const uint4*)(&Ks[(kb * 16 + c16) * KSTR + ks * 32 + q4 * 8]);
+          st[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka.v, qf[gi][ks].v, st[kb], 0, 0, 0);
+        }
+      }
+      float mt = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float sv = valid ? st[kb][e] * scale : -INFINITY;
+          st[kb][e] = sv;
+          mt = fmaxf(mt, sv);
+        }
+      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      const float m_new = fmaxf(m_run[gi], mt);
+      const float alpha = m_new == -INFINITY ? 1.0f : expf(m_run[gi] - m_new);
+      float ls = 0.f;
+      U4 pa[2];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float pv = valid ? expf(st[kb][e] - m_new) : 0.f;
+          ls += pv;
+          pa[kb >> 1].h[(kb & 1) * 4 + e] = f2bf(pv);
+        }
+      ls += __shfl_xor(ls, 16, 64);
+      ls += __shfl_xor(ls, 32, 64);
+      l_run[gi] = l_run[gi] * alpha + ls;
+      m_run[gi] = m_new;
+      // rescale O rows 4*q4 + e by their row's alpha (held by lane 4*q4 + e)
+      float al[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) al[e] = __shfl(alpha, q4 * 4 + e, 64);
+#pragma unroll
+      for (int db = 0; db < 8; ++db)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[gi][db][e] *= al[e];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+          const bf16_t* vr = &Vt[(db * 16 + c16) * VSTR + 32 * j + 4 * q4];
+          U4 vb;
+          const uint2 lo = *(const uint2*)vr;
+          const uint2 hi = *(const uint2*)(vr + 16);
+          vb.u = make_uint4(lo.x, lo.y, hi.x, hi.y);
+          o[gi][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[j].v, vb.v, o[gi][db], 0, 0, 0);
+        }
       }
     }
     __syncthreads();
   }
-  T* out = (T*)a.out + (size_t)r * a.H * HD + h * HD;
-  const float inv = 1.0f / l_run;
+
+  // partials: (m, l) from the lane holding the row, O rows 4*q4 + e
 #pragma unroll
-  for (int j = 0; j < NPL; ++j) {
-    const int d = lane + 64 * j;
-    if (d < HD) st_f(out + d, o[j] * inv);
+  for (int gi = 0; gi < 2; ++gi) {
+    if (!gon[gi]) continue;
+    const int g = wave + 4 * gi;
+    if (lane < 16) {
+      const int rl = g * 16 + c16;
+      if (rl < nrows) {
+        float* pm = a.part_ml + (((size_t)split * a.rows + row0 + rl) * a.H + h) * 2;
+        pm[0] = m_run[gi];
+        pm[1] = l_run[gi];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int rl = g * 16 + q4 * 4 + e;
+      if (rl >= nrows) continue;
+      float* po = a.part_o + (((size_t)split * a.rows + row0 + rl) * a.H + h) * 128;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) po[db * 16 + c16] = o[gi][db][e];
+    }
   }
 }
 
@@ -210,13 +489,33 @@ __global__ __launch_bounds__(256) void k_argmax(const float* logits, int V, int3
   if (tid == 0) out[m] = si[0];
 }
 
+
 }  // namespace
+
+int attn_chunk(int ctx, int dtype, int hd) {
+  if (dtype != LA_BF16 || hd != 128) return 0;
+  return ctx <= 1024 ? 128 : ctx <= 4096 ? 256 : 512;
+}
+
+size_t attn_part_floats(int nsplit, int rows, int H, int hd) {
+  return (size_t)nsplit * rows * H * (hd + 2) + (size_t)rows * H * (hd + 2);
+}
 
 hipError_t launch_attention(const AttnDesc& a, int dtype, hipStream_t st) {
   dim3 grid(a.H, a.rows);
+  if (a.chunk > 0) {
+    if (dtype != LA_BF16 || a.hd != 128 || a.chunk % AT || a.nsplit < 1)
+      return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_attn_bulk, dim3(a.H, a.nsplit, (a.rows + 127) / 128), dim3(256), 0, st,
+                       a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_attn_tail<bf16_t, 128>), grid, dim3(64), 0, st, a);
+    return hipGetLastError();
+  }
 #define LA_ATTN_CASE(T, HD)                                                  \
   if (a.hd == HD) {                                                          \
-    hipLaunchKernelGGL((k_attn<T, HD>), grid, dim3(64), 0, st, a);           \
+    hipLaunchKernelGGL((k_attn_tail<T, HD>), grid, dim3(64), 0, st, a);      \
     return hipGetLastError();                                                \
   }
   if (dtype == LA_BF16) {

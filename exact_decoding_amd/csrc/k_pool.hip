@@ -226,7 +226,36 @@ __global__ void k_fill_i32(int32_t* p, int32_t v, size_t n) {
   if (i < n) p[i] = v;
 }
 
+// Streaming read: every thread XORs 16-byte words with a grid stride; the
+// per-block XOR goes to out[block] so the loads are not dead.
+__global__ __launch_bounds__(256) void k_probe_read(const uint4* __restrict__ buf, size_t n16,
+                                                    uint32_t* out) {
+  uint32_t acc = 0;
+  const size_t stride = (size_t)gridDim.x * 256 * 4;
+  for (size_t i = (size_t)blockIdx.x * 256 * 4 + threadIdx.x; i < n16; i += stride) {
+    uint4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = i + u * 256 < n16 ? buf[i + u * 256] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  __shared__ uint32_t red[256];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (threadIdx.x < s) red[threadIdx.x] ^= red[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[blockIdx.x] = red[0];
+}
+
 }  // namespace
+
+hipError_t launch_probe_read(const void* buf, size_t bytes, uint32_t* out, hipStream_t st) {
+  hipLaunchKernelGGL(k_probe_read, dim3(LA_PROBE_BLOCKS), dim3(256), 0, st, (const uint4*)buf, bytes / 16,
+                     out);
+  return hipGetLastError();
+}
 
 hipError_t launch_gather(const PoolDesc& pool, const StepIO& io, const RowLayout& lay,
                          hipStream_t st) {

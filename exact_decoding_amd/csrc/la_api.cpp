@@ -74,7 +74,7 @@ struct WsPlan {
 };
 
 struct Views {
-  size_t x, h, q, att, act, part, logits, amax, kc, vc, kb, vb, rope, pool_tok, pool_cnt,
+  size_t x, h, q, att, att_part, act, part, logits, amax, kc, vc, kb, vb, rope, pool_tok, pool_cnt,
       pool_head, win, cand, ids, pos, prompt, st, total;
 };
 
@@ -83,6 +83,7 @@ struct Shape {
   int M, rows_cap, ld_ctx;
   int N, W, G, cap;
   int S_qkv, S_o, S_gu, S_d;
+  int att_chunk, att_nsplit;  // MFMA-attention chunking (0 = per-row kernel only)
 };
 
 Shape make_shape(const la_model* m, const la_decode_params* p) {
@@ -103,6 +104,8 @@ Shape make_shape(const la_model* m, const la_decode_params* p) {
   s.S_o = gemm_splits(s.d, s.H * s.hd, s.dt);
   s.S_gu = gemm_splits(2 * s.F, s.d, s.dt);
   s.S_d = gemm_splits(s.d, s.F, s.dt);
+  s.att_chunk = attn_chunk(s.ld_ctx, s.dt, s.hd);
+  s.att_nsplit = s.att_chunk ? (s.ld_ctx + s.att_chunk - 1) / s.att_chunk : 0;
   return s;
 }
 
@@ -125,6 +128,7 @@ Views plan_views(const Shape& s) {
   v.h = w.take(R * s.d * es);
   v.q = w.take(R * s.H * s.hd * es);
   v.att = w.take(R * s.H * s.hd * es);
+  v.att_part = w.take((s.att_chunk ? attn_part_floats(s.att_nsplit, (int)R, s.H, s.hd) : 1) * 4);
   v.act = w.take(R * s.F * es);
   v.part = w.take(part);
   v.logits = w.take((size_t)s.M * s.V * 4);
@@ -279,6 +283,8 @@ int enqueue_forward(la_session* ss, int rows, bool mode_prefill) {
   const double att_flops = 4.0 * s.H * s.hd * att_keys;
   LA_KP(LA_PROF_NORM, R * D * (ES + 4.0), 0, launch_embed(ids, m->emb, x, rows, s.d, dt, st),
         "embed");
+  LA_KP(LA_PROF_NORM, R * D * (ES + 4.0), 0,
+        launch_rmsnorm(x, m->layers[0].attn_norm, h, rows, s.d, eps, dt, st), "rmsnorm_attn");
   for (int l = 0; l < s.L; ++l) {
     const LayerW& w = m->layers[l];
     char* kc = ss->at<char>(ss->v.kc) + (size_t)l * s.Hkv * s.ld_ctx * s.hd * es;
@@ -286,8 +292,6 @@ int enqueue_forward(la_session* ss, int rows, bool mode_prefill) {
     char* kb = ss->at<char>(ss->v.kb) + (size_t)l * s.M * s.Hkv * s.hd * es;
     char* vb = ss->at<char>(ss->v.vb) + (size_t)l * s.M * s.Hkv * s.hd * es;
 
-    LA_KP(LA_PROF_NORM, R * D * (ES + 4.0), 0,
-          launch_rmsnorm(x, w.attn_norm, h, rows, s.d, eps, dt, st), "rmsnorm_attn");
     GemmDesc g{};
     g.x = h; g.rows = rows; g.rows_pad = rows; g.K = s.d; g.nseg = 3;
     g.seg[0] = {w.wq, s.H * s.hd};
@@ -313,6 +317,15 @@ int enqueue_forward(la_session* ss, int rows, bool mode_prefill) {
     a.rows = rows; a.H = s.H; a.Hkv = s.Hkv; a.hd = s.hd; a.ld_ctx = s.ld_ctx;
     a.causal_cache = mode_prefill ? 1 : 0;
     a.lay = ss->lay;
+    a.D = s.N - 1;
+    a.chunk = s.att_chunk;
+    a.nsplit = s.att_nsplit;
+    if (a.chunk) {
+      a.part_o = ss->at<float>(ss->v.att_part);
+      a.part_ml = a.part_o + (size_t)a.nsplit * rows * s.H * s.hd;
+      a.tail_o = a.part_ml + (size_t)a.nsplit * rows * s.H * 2;
+      a.tail_ml = a.tail_o + (size_t)rows * s.H * s.hd;
+    }
     LA_KP(LA_PROF_ATTN, att_bytes, att_flops, launch_attention(a, dt, st), "attention");
 
     g = GemmDesc{};
@@ -320,11 +333,10 @@ int enqueue_forward(la_session* ss, int rows, bool mode_prefill) {
     g.seg[0] = {w.wo, s.d}; g.N = s.d; g.S = s.S_o; g.part = part;
     LA_KP(LA_PROF_GEMM, gemm_bytes(s.d, s.H * s.hd), 2.0 * R * s.d * s.H * s.hd,
           launch_gemm(g, dt, st), "gemm_o");
-    LA_KP(LA_PROF_EPI, R * D * (4.0 * s.S_o + 8.0), 0,
-          launch_resid_epi(part, s.S_o, rows, s.d, rows, x, st), "resid_o");
+    LA_KP(LA_PROF_EPI, R * D * (4.0 * s.S_o + 8.0 + ES), 0,
+          launch_resid_norm(part, s.S_o, rows, s.d, rows, x, w.mlp_norm, h, eps, dt, st),
+          "resid_o_norm");
 
-    LA_KP(LA_PROF_NORM, R * D * (ES + 4.0), 0,
-          launch_rmsnorm(x, w.mlp_norm, h, rows, s.d, eps, dt, st), "rmsnorm_mlp");
     g = GemmDesc{};
     g.x = h; g.rows = rows; g.rows_pad = rows; g.K = s.d; g.nseg = 2;
     g.seg[0] = {w.wg, s.F}; g.seg[1] = {w.wu, s.F};
@@ -339,8 +351,11 @@ int enqueue_forward(la_session* ss, int rows, bool mode_prefill) {
     g.seg[0] = {w.wd, s.d}; g.N = s.d; g.S = s.S_d; g.part = part;
     LA_KP(LA_PROF_GEMM, gemm_bytes(s.d, s.F), 2.0 * R * s.d * s.F, launch_gemm(g, dt, st),
           "gemm_down");
-    LA_KP(LA_PROF_EPI, R * D * (4.0 * s.S_d + 8.0), 0,
-          launch_resid_epi(part, s.S_d, rows, s.d, rows, x, st), "resid_down");
+    // the next layer's attention norm, or the final norm after the last layer
+    const void* gnext = l + 1 < s.L ? m->layers[l + 1].attn_norm : m->final_norm;
+    LA_KP(LA_PROF_EPI, R * D * (4.0 * s.S_d + 8.0 + ES), 0,
+          launch_resid_norm(part, s.S_d, rows, s.d, rows, x, gnext, h, eps, dt, st),
+          "resid_down_norm");
   }
   return LA_OK;
 }
@@ -368,8 +383,6 @@ int enqueue_step(la_session* ss) {
   const la_model* m = ss->m;
   float* x = ss->at<float>(ss->v.x);
   void* h = ss->at(ss->v.h);
-  LA_KP(LA_PROF_NORM, R * s.d * (ES + 4.0), 0,
-        launch_rmsnorm(x, m->final_norm, h, s.M, s.d, m->d.norm_eps, dt, st), "rmsnorm_final");
   GemmDesc g{};
   g.x = h; g.rows = s.M; g.rows_pad = s.M; g.K = s.d; g.nseg = 1;
   g.seg[0] = {m->lm_head, s.V}; g.N = s.V; g.S = 1;
@@ -668,10 +681,20 @@ int la_debug_logits(const la_session* s, float* out, int32_t rows) {
   return LA_OK;
 }
 
+size_t la_kernel_attention_ws_bytes(int32_t ld_ctx, int32_t H, int32_t hd, int32_t N, int32_t W,
+                                    int32_t G, int32_t dtype) {
+  if (ld_ctx < 0 || H < 1 || N < 2 || W < 0 || G < 0) return 0;
+  const int chunk = attn_chunk(ld_ctx, dtype, hd);
+  if (!chunk) return 0;
+  const int M = 1 + (W + G) * (N - 1);
+  const int nsplit = (ld_ctx + chunk - 1) / chunk;
+  return attn_part_floats(nsplit > 0 ? nsplit : 1, M, H, hd) * 4;
+}
+
 int la_kernel_attention(const void* q, const void* k_cache, const void* v_cache, int32_t P,
                         int32_t ld_ctx, const void* k_blk, const void* v_blk, void* out, int32_t H,
                         int32_t Hkv, int32_t hd, int32_t N, int32_t W, int32_t G, int32_t dtype,
-                        void* hip_stream) {
+                        void* ws, size_t ws_bytes, void* hip_stream) {
   if (!q || !k_blk || !v_blk || !out) return fail(LA_EINVAL, "null pointer");
   if (P > 0 && (!k_cache || !v_cache)) return fail(LA_EINVAL, "null cache");
   if (P < 0 || ld_ctx < P) return fail(LA_EINVAL, "need 0 <= P <= ld_ctx");
@@ -688,7 +711,37 @@ int la_kernel_attention(const void* q, const void* k_cache, const void* v_cache,
   a.rows = (int)M; a.H = H; a.Hkv = Hkv; a.hd = hd; a.ld_ctx = ld_ctx;
   a.causal_cache = 0;
   a.lay = RowLayout{N, W, G, (int)M};
+  a.D = N - 1;
+  a.chunk = attn_chunk(ld_ctx, dtype, hd);
+  if (a.chunk) {
+    a.nsplit = (ld_ctx + a.chunk - 1) / a.chunk;
+    if (a.nsplit < 1) a.nsplit = 1;
+    const size_t need = attn_part_floats(a.nsplit, (int)M, H, hd) * 4;
+    if (!ws || ws_bytes < need) return fail(LA_ENOMEM, "attention workspace too small");
+    a.part_o = (float*)ws;
+    a.part_ml = a.part_o + (size_t)a.nsplit * M * H * hd;
+    a.tail_o = a.part_ml + (size_t)a.nsplit * M * H * 2;
+    a.tail_ml = a.tail_o + (size_t)M * H * hd;
+  }
   LA_HIP(launch_attention(a, dtype, (hipStream_t)hip_stream));
+  return LA_OK;
+}
+
+int la_probe_read(const void* buf, size_t bytes, uint32_t* out, void* hip_stream) {
+  if (!buf || !out || bytes % 16) return fail(LA_EINVAL, "need buffers and bytes % 16 == 0");
+  LA_HIP(launch_probe_read(buf, bytes, out, (hipStream_t)hip_stream));
+  return LA_OK;
+}
+
+size_t la_packed_bytes(int32_t N, int32_t K) {
+  if (N < 1 || K < 64 || K % 64) return 0;
+  return packed_bytes(N, K);
+}
+
+int la_pack_weight(const void* src, int32_t N, int32_t K, void* dst, void* hip_stream) {
+  if (!src || !dst) return fail(LA_EINVAL, "null pointer");
+  if (N < 1 || K < 64 || K % 64) return fail(LA_EINVAL, "need N >= 1 and K a multiple of 64");
+  LA_HIP(launch_pack(src, N, K, dst, (hipStream_t)hip_stream));
   return LA_OK;
 }
 

@@ -74,6 +74,8 @@ struct GemmDesc {
 };
 
 int gemm_splits(int N, int K, int dtype);
+size_t packed_bytes(int N, int K);
+hipError_t launch_pack(const void* src, int N, int K, void* dst, hipStream_t st);
 hipError_t launch_gemm(const GemmDesc& g, int dtype, hipStream_t st);
 
 // epilogues of the split GEMM
@@ -90,6 +92,8 @@ struct QkvEpi {
 hipError_t launch_qkv_epi(const QkvEpi& e, int dtype, hipStream_t st);
 hipError_t launch_resid_epi(const float* part, int S, int rows_pad, int N, int rows, float* x,
                             hipStream_t st);
+hipError_t launch_resid_norm(const float* part, int S, int rows_pad, int d, int rows, float* x,
+                             const void* g, void* h, float eps, int dtype, hipStream_t st);
 hipError_t launch_silu_epi(const float* part, int S, int rows_pad, int F, int rows, void* act,
                            int dtype, hipStream_t st);
 hipError_t launch_sum_epi(const float* part, int S, int rows_pad, int N, int rows, float* y,
@@ -116,8 +120,21 @@ struct AttnDesc {
   int rows, H, Hkv, hd, ld_ctx;
   int causal_cache;    // 1: every key 0..pos(row) is in the cache (prefill)
   RowLayout lay;
+  // Split of each row's keys: the committed tiles [0, F) go through the MFMA
+  // kernel in chunks of `chunk` positions, [F, pos] through the per-row
+  // kernel; F = min(floor((pos - D) / 64) * 64, floor(P / 64) * 64).
+  // chunk == 0: no MFMA part (F = 0).
+  int D;
+  int chunk;
+  int nsplit;          // chunks allocated in part_* (grid of the MFMA kernel)
+  float* part_o;       // [nsplit][rows][H][hd] unnormalised outputs
+  float* part_ml;      // [nsplit][rows][H][2] running max, sum
+  float* tail_o;       // [rows][H][hd]
+  float* tail_ml;      // [rows][H][2]
 };
 hipError_t launch_attention(const AttnDesc& a, int dtype, hipStream_t st);
+int attn_chunk(int ctx, int dtype, int hd);
+size_t attn_part_floats(int nsplit, int rows, int H, int hd);
 
 // lookahead bookkeeping kernels
 struct PoolDesc {
@@ -148,5 +165,6 @@ struct KvCommit {
 hipError_t launch_kv_commit(const KvCommit& c, int dtype, hipStream_t st);
 hipError_t launch_pool_seed(const PoolDesc& pool, DevState* st, const int32_t* prompt, int n,
                             hipStream_t st_);
+hipError_t launch_probe_read(const void* buf, size_t bytes, uint32_t* out, hipStream_t st);
 hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t st);
 hipError_t launch_fill_bytes0(void* p, size_t n, hipStream_t st);

@@ -12,6 +12,22 @@ def _torch():
     return torch
 
 
+PACKED = ("wq", "wk", "wv", "wo", "wg", "wu", "wd", "lm_head")
+
+
+def pack(t, stream=None):
+    """bf16 [N][K] device tensor -> packed-layout device tensor (see la.h)."""
+    torch = _torch()
+    N, K = t.shape
+    dst = torch.empty(B.la_packed_bytes(N, K), dtype=torch.uint8, device=t.device)
+    B.la_pack_weight(t, N, K, dst, stream)
+    return dst
+
+
+def is_packed_name(name: str) -> bool:
+    return name.split(".")[-1] in PACKED
+
+
 def upload(arr: np.ndarray, device: str = "cuda"):
     """numpy weight (float32, or uint16 bf16 bit patterns) -> torch device tensor."""
     torch = _torch()
@@ -30,9 +46,17 @@ class Model:
         torch = _torch()
         self.shape = shape
         self.device = device
-        self.tensors = [w if isinstance(w, torch.Tensor) else upload(w, device) for w in weights]
         self.stream = stream if stream is not None else torch.cuda.Stream(device=device)
         self.dtype = B.LA_BF16 if shape.dtype == "bf16" else B.LA_F32
+        import synth
+        names = synth.weight_names(shape)
+        self.tensors = []
+        for name, w in zip(names, weights):
+            t = w if isinstance(w, torch.Tensor) else upload(w, device)
+            if self.dtype == B.LA_BF16 and is_packed_name(name) and t.dtype == torch.bfloat16:
+                torch.cuda.synchronize(device)
+                t = pack(t)
+            self.tensors.append(t)
         desc = B.ModelDesc(shape.n_layers, shape.d_model, shape.n_heads, shape.n_kv_heads,
                            shape.head_dim, shape.d_ff, shape.vocab, shape.rope_theta,
                            shape.norm_eps, self.dtype)

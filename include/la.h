@@ -92,14 +92,28 @@ typedef struct {
 typedef struct la_model la_model;
 typedef struct la_session la_session;
 
+/* Packed bf16 weight layout (what la_model_load and la_kernel_gemm take for
+ * the projection and LM-head matrices of bf16 models).  A row-major
+ * W[N][K] (K a multiple of 64) is stored as ceil(N/16) stripes of 16 rows;
+ * stripe s holds K/64 blocks of 2048 bytes, block c holding
+ *   element (j, lane, e) = W[16s + lane%16][64c + 32j + 8(lane/16) + e]
+ * at byte offset ((s*(K/64) + c)*2 + j)*1024 + lane*16 + e*2, for j in {0,1},
+ * lane in [0,64), e in [0,8); rows >= N are zero.  Every 1 KB is one MFMA
+ * B operand of 64 lanes, so a GEMM streams each stripe sequentially. */
+size_t la_packed_bytes(int32_t N, int32_t K);
+/* Pack a row-major bf16 W[N][K] (device) into `dst` (device, la_packed_bytes
+ * bytes).  Enqueued on `hip_stream`. */
+int la_pack_weight(const void* src, int32_t N, int32_t K, void* dst, void* hip_stream);
+
 /* Register a model.  `dev_weights` holds n_weights = 3 + 9*n_layers device
  * pointers, owned by the caller, in this order:
  *   emb [vocab][d], then per layer: attn_norm [d], wq [H*hd][d],
  *   wk [Hkv*hd][d], wv [Hkv*hd][d], wo [d][H*hd], mlp_norm [d],
  *   wg [d_ff][d], wu [d_ff][d], wd [d][d_ff], then final_norm [d],
  *   lm_head [vocab][d].
- * Matrices are row-major [out][in] of the model dtype.  They must stay
- * valid until la_model_free.  bf16 models need d, H*hd and d_ff to be
+ * fp32 models: matrices row-major [out][in].  bf16 models: wq, wk, wv, wo,
+ * wg, wu, wd and lm_head in the packed layout above (la_pack_weight); emb
+ * and the norm gains row-major.  They must stay valid until la_model_free.  bf16 models need d, H*hd and d_ff to be
  * multiples of 64 and H*hd, Hkv*hd multiples of 128; head_dim <= 128 and
  * even.  *out receives a library-owned handle. */
 int la_model_load(const la_model_desc* d, const void* const* dev_weights, int n_weights,
@@ -185,21 +199,34 @@ const char* la_last_error(void);
  *   k_blk, v_blk     [M][Hkv*hd]        device, dtype
  *   out     [M][H*hd]          device, dtype (written)
  * with M = 1 + (W+G)(N-1).  Row positions are P + offset (row layout of
- * la_step).  Enqueued on `hip_stream`; does not synchronise. */
+ * la_step).  ws: device scratch of ws_bytes >= la_kernel_attention_ws_bytes.
+ * Enqueued on `hip_stream`; does not synchronise. */
 int la_kernel_attention(const void* q, const void* k_cache, const void* v_cache, int32_t P,
                         int32_t ld_ctx, const void* k_blk, const void* v_blk, void* out,
                         int32_t H, int32_t Hkv, int32_t hd, int32_t N, int32_t W, int32_t G,
-                        int32_t dtype, void* hip_stream);
+                        int32_t dtype, void* ws, size_t ws_bytes, void* hip_stream);
+/* Device scratch bytes la_kernel_attention needs (partial softmax states of
+ * the committed-prefix chunks); 0 when it needs none. */
+size_t la_kernel_attention_ws_bytes(int32_t ld_ctx, int32_t H, int32_t hd, int32_t N, int32_t W,
+                                    int32_t G, int32_t dtype);
 
 /* The projection GEMM on its own (test / benchmark hook):
  * y[m][n] = sum_k x[m][k] * w[n][k] in fp32, with the same split and
  * summation order the step uses for an N x K weight.
- *   x [M][K], w [N][K] device, dtype; y [M][N] device fp32 (written);
+ *   x [M][K] device, dtype; w device: packed (bf16) or [N][K] (fp32);
+ *   y [M][N] device fp32 (written);
  *   ws device scratch of ws_bytes >= la_kernel_gemm_ws_bytes(M, K, N).
  * M >= 1; K a multiple of 64 for bf16.  Enqueued on `hip_stream`. */
 int la_kernel_gemm(const void* x, int32_t M, int32_t K, const void* w, int32_t N, float* y,
                    int32_t dtype, void* ws, size_t ws_bytes, void* hip_stream);
 size_t la_kernel_gemm_ws_bytes(int32_t M, int32_t K, int32_t N);
+
+/* HBM read probe (benchmark hook): reads `bytes` (a multiple of 16) from the
+ * device buffer `buf` with 16-byte loads across the whole chip and writes one
+ * checksum word per workgroup to `out` (device, LA_PROBE_BLOCKS uint32);
+ * measures the achievable read bandwidth.  Enqueued on `hip_stream`. */
+#define LA_PROBE_BLOCKS 2048
+int la_probe_read(const void* buf, size_t bytes, uint32_t* out, void* hip_stream);
 
 #ifdef __cplusplus
 }

@@ -178,6 +178,7 @@ def prompt_zipf_spans(vocab: int, length: int = 128, n_spans: int = 3, span: int
     toks = _zipf_ids(g, length, vocab, a)
     nblk = length // span
     half = nblk // 2
+    n_spans = min(n_spans, half, nblk - half)
     src = g.choice(half, size=n_spans, replace=False)
     dst = half + g.choice(nblk - half, size=n_spans, replace=False)
     for s_, d_ in zip(src, dst):

@@ -23,15 +23,46 @@ def _bf16(a, seed_scale=1.0):
     return torch.from_numpy(np.asarray(a, np.float32) * seed_scale).to(torch.bfloat16).to(DEV)
 
 
-def _gemm(x, w, dtype=B.LA_BF16):
+def _pack(w):
+    N, K = w.shape
+    dst = torch.empty(B.la_packed_bytes(N, K), dtype=torch.uint8, device=DEV)
+    B.la_pack_weight(w, N, K, dst, None)
+    torch.cuda.synchronize()
+    return dst
+
+
+def _gemm(x, w, dtype=B.LA_BF16, wp=None):
     M, K = x.shape
     N = w.shape[0]
+    if dtype == B.LA_BF16 and wp is None:
+        wp = _pack(w)
     y = torch.empty((M, N), dtype=torch.float32, device=DEV)
     nb = B.la_kernel_gemm_ws_bytes(M, K, N)
     ws = torch.empty(max(nb, 4), dtype=torch.uint8, device=DEV)
-    B.la_kernel_gemm(x, M, K, w, N, y, dtype, ws, None)
+    B.la_kernel_gemm(x, M, K, wp if dtype == B.LA_BF16 else w, N, y, dtype, ws, None)
     torch.cuda.synchronize()
     return y
+
+
+def test_pack_layout():
+    """The packed layout places W[16s + lane%16][64c + 32j + 8(lane/16) + e]
+    at element ((s*(K/64) + c)*2 + j)*512 + lane*8 + e; rows past N are 0."""
+    N, K = 37, 128
+    w = torch.arange(N * K, dtype=torch.float32).reshape(N, K).to(torch.bfloat16).to(DEV)
+    got = _pack(w).view(torch.bfloat16).float().cpu().numpy()
+    wf = w.float().cpu().numpy()
+    nch = K // 64
+    ref = np.zeros(((N + 15) // 16) * 16 * K, dtype=np.float32)
+    for s_ in range((N + 15) // 16):
+        for c in range(nch):
+            for j in range(2):
+                for lane in range(64):
+                    row = 16 * s_ + lane % 16
+                    k = 64 * c + 32 * j + 8 * (lane // 16)
+                    base = ((s_ * nch + c) * 2 + j) * 512 + lane * 8
+                    if row < N:
+                        ref[base:base + 8] = wf[row, k:k + 8]
+    np.testing.assert_array_equal(got, ref)
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 256, 384), (17, 512, 640), (121, 4096, 4096),
@@ -67,11 +98,12 @@ def test_gemm_rows_bit_identical_across_batch():
     K, N = 4096, 4096
     x = _bf16(rng.standard_normal((121, K)))
     w = _bf16(rng.standard_normal((N, K)) * 0.02)
-    full = _gemm(x, w)
+    wp = _pack(w)
+    full = _gemm(x, w, wp=wp)
     for r in [0, 1, 15, 16, 63, 120]:
-        one = _gemm(x[r:r + 1].contiguous(), w)
+        one = _gemm(x[r:r + 1].contiguous(), w, wp=wp)
         assert torch.equal(one[0], full[r]), r
-    part = _gemm(x[5:22].contiguous(), w)
+    part = _gemm(x[5:22].contiguous(), w, wp=wp)
     assert torch.equal(part, full[5:22])
 
 
@@ -93,13 +125,17 @@ def _rand_attn(P, H, Hkv, hd, N, W, G, dtype, seed, ld_ctx=None):
 def _run_attn(dev, P, ld_ctx, H, Hkv, hd, N, W, G, dtype, tdt, M):
     q, kc, vc, kb, vb = dev
     out = torch.empty((M, H * hd), dtype=tdt, device=DEV)
-    B.la_kernel_attention(q, kc, vc, P, ld_ctx, kb, vb, out, H, Hkv, hd, N, W, G, dtype, None)
+    nb = B.la_kernel_attention_ws_bytes(ld_ctx, H, hd, N, W, G, dtype)
+    ws = torch.empty(max(nb, 4), dtype=torch.uint8, device=DEV)
+    B.la_kernel_attention(q, kc, vc, P, ld_ctx, kb, vb, out, H, Hkv, hd, N, W, G, dtype, ws, None)
     torch.cuda.synchronize()
     return out
 
 
 @pytest.mark.parametrize("P,H,Hkv,hd,N,W,G,dtype", [
     (37, 4, 2, 128, 3, 4, 4, B.LA_BF16),
+    (300, 8, 2, 128, 4, 5, 3, B.LA_BF16),
+    (1500, 8, 8, 128, 3, 2, 2, B.LA_BF16),
     (0, 4, 4, 128, 4, 3, 2, B.LA_BF16),
     (200, 4, 4, 16, 3, 4, 4, B.LA_F32),
     (512, 32, 32, 128, 5, 15, 15, B.LA_BF16),
@@ -118,7 +154,7 @@ def test_attention_matches_oracle(P, H, Hkv, hd, N, W, G, dtype):
     assert np.abs(got - ref).max() < tol
 
 
-@pytest.mark.parametrize("P", [5, 63, 64, 130])
+@pytest.mark.parametrize("P", [5, 63, 64, 130, 300, 1100])
 def test_attention_verification_row_equals_ar_query(P):
     """Verification row (g, i) == one query at P+i over a cache holding the
     prefix and the row's chain (what an autoregressive step computes)."""
@@ -139,8 +175,12 @@ def test_attention_verification_row_equals_ar_query(P):
         last = chain[-1]
         q1 = q[r:r + 1].contiguous()
         out1 = torch.empty((1, H * hd), dtype=tdt, device=DEV)
+        # the autoregressive query uses the same tail depth (N - 1) as the
+        # lookahead session it is compared with
+        nb = B.la_kernel_attention_ws_bytes(ld, H, hd, N, 0, 0, B.LA_BF16)
+        ws = torch.empty(max(nb, 4), dtype=torch.uint8, device=DEV)
         B.la_kernel_attention(q1, kc2, vc2, P + i, ld, kb[last:last + 1].contiguous(),
-                              vb[last:last + 1].contiguous(), out1, H, Hkv, hd, 2, 0, 0,
-                              B.LA_BF16, None)
+                              vb[last:last + 1].contiguous(), out1, H, Hkv, hd, N, 0, 0,
+                              B.LA_BF16, ws, None)
         torch.cuda.synchronize()
         assert torch.equal(out1[0], out[r]), (r, g, i)

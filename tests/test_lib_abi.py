@@ -101,9 +101,12 @@ def test_kernel_hooks_validate():
     lib = B.load_library()
     P = ctypes.c_void_p(0x1000)
     # bad head_dim / N
-    assert lib.la_kernel_attention(P, P, P, 4, 8, P, P, P, 4, 4, 100, 3, 2, 2, 1, None) == B.LA_EINVAL
-    assert lib.la_kernel_attention(P, P, P, 4, 8, P, P, P, 4, 4, 128, 1, 2, 2, 1, None) == B.LA_EINVAL
-    assert lib.la_kernel_attention(P, P, P, 9, 8, P, P, P, 4, 4, 128, 3, 2, 2, 1, None) == B.LA_EINVAL
+    assert lib.la_kernel_attention(P, P, P, 4, 8, P, P, P, 4, 4, 100, 3, 2, 2, 1, None, 0, None) == B.LA_EINVAL
+    assert lib.la_kernel_attention(P, P, P, 4, 8, P, P, P, 4, 4, 128, 1, 2, 2, 1, None, 0, None) == B.LA_EINVAL
+    assert lib.la_kernel_attention(P, P, P, 9, 8, P, P, P, 4, 4, 128, 3, 2, 2, 1, None, 0, None) == B.LA_EINVAL
+    # bf16 head_dim 128 needs the partial-state scratch
+    assert B.la_kernel_attention_ws_bytes(512, 32, 128, 5, 15, 15, B.LA_BF16) > 0
+    assert lib.la_kernel_attention(P, P, P, 4, 8, P, P, P, 4, 4, 128, 3, 2, 2, 1, None, 0, None) == B.LA_ENOMEM
     # bf16 GEMM needs K % 64 == 0
     assert lib.la_kernel_gemm(P, 4, 100, P, 64, P, B.LA_BF16, None, 0, None) == B.LA_EINVAL
     assert B.la_kernel_gemm_ws_bytes(121, 4096, 4096) > 0
