@@ -20,7 +20,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 namespace {
 
 union U4 {
-  uint4 u;
+  u32x4_t u;
   bf16x8_t v;
   bf16_t h[8];
 };
@@ -73,7 +73,7 @@ __device__ __forceinline__ float dot_q(const float* qs, const bf16_t* k) {
   float a[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int d0 = 0; d0 < HD; d0 += 8) {
-    const uint4 u = *(const uint4*)(k + d0);
+    const u32x4_t u = *(const u32x4_t*)(k + d0);
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -120,15 +120,42 @@ __device__ __forceinline__ int row_pos(const AttnDesc& a, int r, int Pc) {
 // block chain above).  Lane j of a tile scores the key at position 64t + j;
 // lanes own output dimensions lane, lane+64 for the P.V sum.  Writes the
 // normalised output when there is no MFMA part, else (m, l, o) partials.
+template <int HD>
+__device__ __forceinline__ float dot_r(const float* qs, const u32x4_t (&k)[HD / 8], bf16_t) {
+  float a[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < HD / 8; ++c) {
+    const uint32_t w[4] = {k[c].x, k[c].y, k[c].z, k[c].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a[(2 * e) & 3] = fmaf(qs[8 * c + 2 * e], __uint_as_float(w[e] << 16), a[(2 * e) & 3]);
+      a[(2 * e + 1) & 3] =
+          fmaf(qs[8 * c + 2 * e + 1], __uint_as_float(w[e] & 0xFFFF0000u), a[(2 * e + 1) & 3]);
+    }
+  }
+  return (a[0] + a[1]) + (a[2] + a[3]);
+}
+template <int HD>
+__device__ __forceinline__ float dot_r(const float* qs, const u32x4_t (&k)[HD / 4], float) {
+  float a[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < HD / 4; ++c) {
+    a[0] = fmaf(qs[4 * c], __uint_as_float(k[c].x), a[0]);
+    a[1] = fmaf(qs[4 * c + 1], __uint_as_float(k[c].y), a[1]);
+    a[2] = fmaf(qs[4 * c + 2], __uint_as_float(k[c].z), a[2]);
+    a[3] = fmaf(qs[4 * c + 3], __uint_as_float(k[c].w), a[3]);
+  }
+  return (a[0] + a[1]) + (a[2] + a[3]);
+}
+
 template <typename T, int HD>
 __global__ __launch_bounds__(64) void k_attn_tail(AttnDesc a) {
-  // keys per pass: two per lane when the staged V rows fit in LDS
-  constexpr int KP = (int)sizeof(T) * HD <= 256 ? 128 : 64;
+  constexpr int NV = HD * (int)sizeof(T) / 16;       // 16-byte words per K / V row
   constexpr int DPL = HD >= 64 ? HD / 64 : 1;        // output dims per lane (contiguous)
   constexpr int VSTRIDE = HD + 16 / (int)sizeof(T);  // padded LDS row of V
   __shared__ float qs[HD];
-  __shared__ float ps[KP];
-  __shared__ __align__(16) T vs[KP * VSTRIDE];
+  __shared__ float ps[AT];
+  __shared__ __align__(16) T vs[AT * VSTRIDE];
   const int h = blockIdx.x, r = blockIdx.y, lane = threadIdx.x;
   const int kvh = h * a.Hkv / a.H;
   const int Pc = a.Pdev ? *a.Pdev : a.P_host;
@@ -141,8 +168,6 @@ __global__ __launch_bounds__(64) void k_attn_tail(AttnDesc a) {
   const T* vc = (const T*)a.vc + (size_t)kvh * a.ld_ctx * HD;
   const T* kb = (const T*)a.kb + kvh * HD;
   const T* vb = (const T*)a.vb + kvh * HD;
-  for (int i = lane; i < HD; i += 64) qs[i] = ld_f(q + i);
-  __syncthreads();
   const float scale = 1.0f / sqrtf((float)HD);
   const int d0 = lane * DPL;
   const bool down = d0 < HD;
@@ -152,59 +177,54 @@ __global__ __launch_bounds__(64) void k_attn_tail(AttnDesc a) {
 #pragma unroll
   for (int j = 0; j < DPL; ++j) o[j] = 0.f;
 
-  // passes over [F, pos] aligned to multiples of KP in absolute position
-  for (int base = (F / KP) * KP; base <= pos; base += KP) {
-    const int lo = base > F ? base : F;
-    const int hi = min(pos, base + KP - 1);
-    float sc[KP / 64];
+  // tiles of 64 absolute positions over [F, pos]; lane j holds key 64t + j
+  for (int t = F / AT; t <= pos / AT; ++t) {
+    const int p = t * AT + lane;
+    const bool on = p >= F && p <= pos;
+    u32x4_t kr[NV], vr[NV];
+    if (on) {
+      const int src = p < P ? -1 : chain_row(r, p - P, a.lay);
+      const u32x4_t* kp = (const u32x4_t*)(src < 0 ? kc + (size_t)p * HD : kb + (size_t)src * ldb);
+      const u32x4_t* vp = (const u32x4_t*)(src < 0 ? vc + (size_t)p * HD : vb + (size_t)src * ldb);
 #pragma unroll
-    for (int u = 0; u < KP / 64; ++u) {
-      const int p = base + u * 64 + lane;
-      sc[u] = -INFINITY;
-      if (p >= lo && p <= hi) {
-        const int src = p < P ? -1 : chain_row(r, p - P, a.lay);
-        const T* kp = src < 0 ? kc + (size_t)p * HD : kb + (size_t)src * ldb;
-        const T* vp = src < 0 ? vc + (size_t)p * HD : vb + (size_t)src * ldb;
+      for (int e = 0; e < NV; ++e) kr[e] = kp[e];
 #pragma unroll
-        for (int e = 0; e < HD * (int)sizeof(T) / 16; ++e)
-          *(uint4*)((char*)(vs + (u * 64 + lane) * VSTRIDE) + 16 * e) = *((const uint4*)vp + e);
-        sc[u] = dot_q<HD>(qs, kp) * scale;
-      }
+      for (int e = 0; e < NV; ++e) vr[e] = vp[e];
     }
-    float mp = sc[0];
+    if (t == F / AT)
+      for (int i = lane; i < HD; i += 64) qs[i] = ld_f(q + i);
+    if (on) {
 #pragma unroll
-    for (int u = 1; u < KP / 64; ++u) mp = fmaxf(mp, sc[u]);
-    mp = wave_max(mp);
-    float lp = 0.f;
-#pragma unroll
-    for (int u = 0; u < KP / 64; ++u) {
-      const float pv = sc[u] == -INFINITY ? 0.f : expf(sc[u] - mp);
-      ps[u * 64 + lane] = pv;
-      lp += pv;
+      for (int e = 0; e < NV; ++e) *(u32x4_t*)((char*)(vs + lane * VSTRIDE) + 16 * e) = vr[e];
     }
-    lp = wave_sum(lp);
     __syncthreads();
-    // P.V over this pass: key j goes to partial j mod 4
+    const float sc = on ? dot_r<HD>(qs, kr, T()) * scale : -INFINITY;
+    const float mp = wave_max(sc);
+    const float pv = on ? expf(sc - mp) : 0.f;
+    ps[lane] = pv;
+    const float lp = wave_sum(pv);
+    __syncthreads();
+    // P.V over this tile: key j goes to partial j mod 4
     float acc[4][DPL];
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int j = 0; j < DPL; ++j) acc[t][j] = 0.f;
+      for (int j = 0; j < DPL; ++j) acc[u][j] = 0.f;
     if (down) {
-      const int n = hi - base + 1;
-      for (int jj = lo - base; jj < n; jj += 4) {
+      const int j0 = F > t * AT ? F - t * AT : 0;
+      const int n = min(AT, pos - t * AT + 1);
+      for (int jj = j0; jj < n; jj += 4) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          if (jj + t < n) {
-            const float w = ps[jj + t];
-            const T* vr = vs + (jj + t) * VSTRIDE + d0;
+        for (int u = 0; u < 4; ++u) {
+          if (jj + u < n) {
+            const float w = ps[jj + u];
+            const T* vrow = vs + (jj + u) * VSTRIDE + d0;
 #pragma unroll
-            for (int j = 0; j < DPL; ++j) acc[t][j] = fmaf(w, ld_f(vr + j), acc[t][j]);
+            for (int j = 0; j < DPL; ++j) acc[u][j] = fmaf(w, ld_f(vrow + j), acc[u][j]);
           }
         }
       }
     }
-    // fold the pass into the running state
     const float mn = fmaxf(m_run, mp);
     const float ca = m_run == -INFINITY ? 0.f : expf(m_run - mn);
     const float cb = expf(mp - mn);
@@ -302,10 +322,10 @@ __global__ __launch_bounds__(256) void k_attn_bulk(AttnDesc a) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       if (gon[gi] && rl < nrows)
-        qf[gi][ks].u = *(const uint4*)((const bf16_t*)a.q + (size_t)r * a.H * 128 + h * 128 +
+        qf[gi][ks].u = *(const u32x4_t*)((const bf16_t*)a.q + (size_t)r * a.H * 128 + h * 128 +
                                        ks * 32 + q4 * 8);
       else
-        qf[gi][ks].u = make_uint4(0, 0, 0, 0);
+        qf[gi][ks].u = u32x4_t{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int db = 0; db < 8; ++db) o[gi][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -324,12 +344,12 @@ __global__ __launch_bounds__(256) void k_attn_bulk(AttnDesc a) {
     // stage K [key][dim] and V^T [dim][key] for positions t0 .. t0+63
     {
       const int key = tid >> 2, seg = tid & 3;  // 32 dims per thread
-      const uint4* src = (const uint4*)(kc + (size_t)(t0 + key) * 128 + seg * 32);
+      const u32x4_t* src = (const u32x4_t*)(kc + (size_t)(t0 + key) * 128 + seg * 32);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) *(uint4*)(&Ks[key * KSTR + seg * 32 + j * 8]) = src[j];
+      for (int j = 0; j < 4; ++j) *(u32x4_t*)(&Ks[key * KSTR + seg * 32 + j * 8]) = src[j];
       const int kp = tid & 31, vs = tid >> 5;  // key pair, 16-dim segment
-      const uint4* v0 = (const uint4*)(vc + (size_t)(t0 + 2 * kp) * 128 + vs * 16);
-      const uint4* v1 = (const uint4*)(vc + (size_t)(t0 + 2 * kp + 1) * 128 + vs * 16);
+      const u32x4_t* v0 = (const u32x4_t*)(vc + (size_t)(t0 + 2 * kp) * 128 + vs * 16);
+      const u32x4_t* v1 = (const u32x4_t*)(vc + (size_t)(t0 + 2 * kp + 1) * 128 + vs * 16);
       U4 a0, a1, b0, b1;
       a0.u = v0[0]; a1.u = v0[1]; b0.u = v1[0]; b1.u = v1[1];
 #pragma unroll
@@ -355,7 +375,7 @@ __global__ __launch_bounds__(256) void k_attn_bulk(AttnDesc a) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
           U4 ka;
-          ka.u = *(const uint4*)(&Ks[(kb * 16 + c16) * KSTR + ks * 32 + q4 * 8]);
+          ka.u = *(const u32x4_t*)(&Ks[(kb * 16 + c16) * KSTR + ks * 32 + q4 * 8]);
           st[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka.v, qf[gi][ks].v, st[kb], 0, 0, 0);
         }
       }
@@ -400,9 +420,9 @@ __global__ __launch_bounds__(256) void k_attn_bulk(AttnDesc a) {
         for (int db = 0; db < 8; ++db) {
           const bf16_t* vr = &Vt[(db * 16 + c16) * VSTR + 32 * j + 4 * q4];
           U4 vb;
-          const uint2 lo = *(const uint2*)vr;
-          const uint2 hi = *(const uint2*)(vr + 16);
-          vb.u = make_uint4(lo.x, lo.y, hi.x, hi.y);
+          const u32x2_t lo = *(const u32x2_t*)vr;
+          const u32x2_t hi = *(const u32x2_t*)(vr + 16);
+          vb.u = u32x4_t{lo.x, lo.y, hi.x, hi.y};
           o[gi][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[j].v, vb.v, o[gi][db], 0, 0, 0);
         }
       }
@@ -469,12 +489,32 @@ __global__ __launch_bounds__(256) void k_argmax(const float* logits, int V, int3
   __shared__ int si[256];
   const int m = blockIdx.x, tid = threadIdx.x;
   const float* row = logits + (size_t)m * V;
-  float bv = -INFINITY;
-  int bi = 0x7fffffff;
-  for (int n = tid; n < V; n += 256) {
-    const float v = row[n];
-    if (v > bv) { bv = v; bi = n; }
+  // eight independent (value, index) chains per thread, combined in order
+  float bv8[8];
+  int bi8[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) { bv8[u] = -INFINITY; bi8[u] = 0x7fffffff; }
+  int n0 = tid;
+  for (; n0 + 7 * 256 < V; n0 += 8 * 256) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = row[n0 + u * 256];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (v[u] > bv8[u]) { bv8[u] = v[u]; bi8[u] = n0 + u * 256; }
   }
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    if (n0 + u * 256 < V) {
+      const float v = row[n0 + u * 256];
+      if (v > bv8[u]) { bv8[u] = v; bi8[u] = n0 + u * 256; }
+    }
+  }
+  float bv = bv8[0];
+  int bi = bi8[0];
+#pragma unroll
+  for (int u = 1; u < 8; ++u)
+    if (bv8[u] > bv || (bv8[u] == bv && bi8[u] < bi)) { bv = bv8[u]; bi = bi8[u]; }
   sv[tid] = bv;
   si[tid] = bi;
   __syncthreads();

@@ -14,9 +14,6 @@
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
-// native 16-byte vector (HIP's uint4 is a struct whose copies can stay in
-// private memory)
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 namespace {
 
@@ -409,8 +406,9 @@ int gemm_splits(int N, int K, int dtype) {
   const int nblk = (N + NWG - 1) / NWG;
   const int nch = K / KC;
   int S = 1;
-  // enough workgroups to cover the 256 CUs, keeping >= 4 chunks per split
-  while (nblk * S < LA_GEMM_TARGET_WG && (S * 2) * 4 <= nch && S < 16) S *= 2;
+  // the largest power-of-two split that keeps the grid within one round of
+  // LA_GEMM_TARGET_WG workgroups (one per CU), with >= 4 chunks per split
+  while (nblk * S * 2 <= LA_GEMM_TARGET_WG && (S * 2) * 4 <= nch && S < 16) S *= 2;
   return S;
 }
 

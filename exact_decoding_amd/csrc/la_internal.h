@@ -7,6 +7,10 @@
 #include "la.h"
 
 typedef uint16_t bf16_t;
+// native 16-byte vector: HIP's uint4 is a struct whose copies the compiler can
+// leave in private memory
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------------------
 // scalar storage types: fp32 or bf16 (round to nearest even on store)
