@@ -46,9 +46,54 @@ def parse():
     ap.add_argument("--max-new", type=int, default=256)
     ap.add_argument("--profile-steps", type=int, default=32)
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
-    ap.add_argument("--cpu-tokens", type=int, default=2)
+    ap.add_argument("--cpu-tokens", type=int, default=48)
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="first run a 1 GiB HBM read (la_probe_read) and a 1 GiB fill, "
+                         "the known-size kernels that scale the PMC byte counters")
     return ap.parse_args()
+
+
+def calibrate():
+    """Known-size kernels: read 1 GiB with la_probe_read, write 1 GiB with a
+    fill.  Returns the measured read bandwidth (GB/s)."""
+    import torch
+    from exact_decoding_amd import binding as B
+    n = 1 << 30
+    buf = torch.empty(n, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    out = torch.zeros(B.LA_PROBE_BLOCKS, dtype=torch.int32, device="cuda")
+    B.la_probe_read(buf, n, out, None)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        B.la_probe_read(buf, n, out, None)
+    e1.record()
+    torch.cuda.synchronize()
+    gbps = 5 * n / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del buf
+    return gbps
+
+
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "k_gemm_bf16_llama7b_lookahead_pmc.md")
+GEMM_SOURCE = os.path.join(ROOT, "exact_decoding_amd", "csrc", "k_gemm.hip")
+
+
+def gemm_traffic():
+    """HBM bytes per k_gemm_bf16 launch from the committed FETCH_SIZE /
+    WRITE_SIZE summary, or None when the kernel source has changed since the
+    counters were taken (or there is no summary)."""
+    import hashlib
+    try:
+        text = open(PMC_SUMMARY).read()
+        src = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    fields = dict(l.split(": ", 1) for l in text.splitlines() if ": " in l)
+    if fields.get("k_gemm.hip sha256", "").strip() != src:
+        return None
+    return float(fields["traffic bytes per launch"])
 
 
 def log(*a):
@@ -122,6 +167,10 @@ def main():
 
     shape = synth.SHAPES[args.shape]
     N, W, G = args.N, args.W, args.G
+    read_gbps = None
+    if args.calibrate:
+        read_gbps = calibrate()
+        log(f"[bench] calibration: 1 GiB read at {read_gbps:.0f} GB/s")
     t0 = time.time()
     log(f"[bench] generating + uploading {shape.name} weights")
     weights_np = []
@@ -202,7 +251,9 @@ def main():
                     agg[k][f] += v[f]
     ses.close()
     P_avg = P_sum / max(n_prof, 1)
-    g = agg["gemm"]
+    # the dominant kernel is the projection GEMM k_gemm_bf16; its launches are
+    # the four projections per layer plus the LM head
+    g = {f: agg["gemm"][f] + agg["lm_head"][f] for f in agg["gemm"]}
     gemm_ms = g["ms"] / g["launches"]
     gemm_bytes = g["bytes"] / g["launches"]
     gemm_gbps = g["bytes"] / (g["ms"] * 1e-3) / 1e9
@@ -244,13 +295,14 @@ def main():
         "lookahead_equals_ar": exact,
         "step_hbm": {"bytes_per_step": step_bytes, "GBps": step_gbps, "frac": step_gbps / HBM_PEAK_GBPS,
                      "P_avg": P_avg},
-        "roofline": {"kernel": "k_gemm_bf16 (QKV/O/gate-up/down projections)", "bound": "hbm",
+        "roofline": {"kernel": "k_gemm_bf16 (QKV, O, gate/up, down projections and LM head)", "bound": "hbm",
                      "achieved": gemm_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": gemm_gbps / HBM_PEAK_GBPS, "traffic": None,
+                     "frac": gemm_gbps / HBM_PEAK_GBPS, "traffic": gemm_traffic(),
                      "avg_launch_ms": gemm_ms, "avg_launch_bytes": gemm_bytes,
                      "mfma_tflops": g["flops"] / (g["ms"] * 1e-3) / 1e12},
         "profile_ms_per_step": breakdown,
         "profile_step_ms_eager": prof_total_ms,
+        "achievable_read_GBps": read_gbps,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -18,6 +18,7 @@ LA_OK, LA_DONE = 0, 1
 LA_EINVAL, LA_ENOMEM, LA_ECTX, LA_EHIP, LA_ESTATE = -1, -2, -3, -4, -5
 LA_F32, LA_BF16 = 0, 1
 LA_MAX_N = 16
+LA_PROBE_BLOCKS = 2048
 LA_PROMPT_REF, LA_AR, LA_NO_GRAPH = 1, 2, 8
 
 EXPORTS = [
@@ -25,6 +26,7 @@ EXPORTS = [
     "la_pool_stats", "la_debug_logits", "la_session_rows", "la_session_free", "la_last_error",
     "la_kernel_attention", "la_kernel_gemm", "la_kernel_gemm_ws_bytes", "la_step_profile",
     "la_kernel_attention_ws_bytes", "la_packed_bytes", "la_pack_weight", "la_probe_read",
+    "la_step_trace", "la_step_trace_bytes",
 ]
 
 PROF_KINDS = ["gemm", "lm_head", "attention", "norm", "epilogue", "argmax", "bookkeeping"]
@@ -98,6 +100,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.la_step_profile.argtypes = [P, ctypes.POINTER(I32), I32, ctypes.POINTER(I32),
                                     ctypes.POINTER(Profile)]
     lib.la_debug_logits.argtypes = [P, ctypes.POINTER(ctypes.c_float), I32]
+    lib.la_step_trace.argtypes = [P, ctypes.POINTER(I32), I32, ctypes.POINTER(I32), P,
+                                  ctypes.c_size_t]
+    lib.la_step_trace_bytes.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
     lib.la_session_rows.argtypes = [P, ctypes.POINTER(I32)]
     lib.la_session_free.argtypes = [P]
     lib.la_session_free.restype = None
@@ -180,6 +185,23 @@ def la_step_profile(session, out_cap: int) -> tuple[int, list[int], dict]:
     prof = Profile()
     rc = _check(lib.la_step_profile(session, buf, out_cap, ctypes.byref(n), ctypes.byref(prof)))
     return rc, list(buf[:n.value]), prof.as_dict()
+
+
+def la_step_trace_bytes(session) -> int:
+    lib = load_library()
+    n = ctypes.c_size_t()
+    _check(lib.la_step_trace_bytes(session, ctypes.byref(n)))
+    return n.value
+
+
+def la_step_trace(session, out_cap: int, trace, nbytes: int) -> tuple[int, list[int]]:
+    """One step with the per-layer trace written to device memory `trace`
+    (a device pointer or a tensor exposing data_ptr())."""
+    lib = load_library()
+    buf = (ctypes.c_int32 * out_cap)()
+    n = ctypes.c_int32()
+    rc = _check(lib.la_step_trace(session, buf, out_cap, ctypes.byref(n), _ptr(trace), nbytes))
+    return rc, list(buf[:n.value])
 
 
 def la_pool_stats(session) -> dict:

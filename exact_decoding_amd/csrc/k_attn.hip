@@ -392,15 +392,21 @@ __global__ __launch_bounds__(256) void k_attn_bulk(AttnDesc a) {
       mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
       const float m_new = fmaxf(m_run[gi], mt);
       const float alpha = m_new == -INFINITY ? 1.0f : expf(m_run[gi] - m_new);
+      // p enters the PV product as the sum of two bf16 values, hi = bf16(p)
+      // and lo = bf16(p - hi) (p - hi is exact in fp32), so the product
+      // carries p to about 2^-17 relative, as an fp32 product would: no
+      // rounding of the probabilities beyond the fp32 arithmetic
       float ls = 0.f;
-      U4 pa[2];
+      U4 pa[2], pl[2];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float pv = valid ? expf(st[kb][e] - m_new) : 0.f;
           ls += pv;
-          pa[kb >> 1].h[(kb & 1) * 4 + e] = f2bf(pv);
+          const uint16_t hb = f2bf(pv);
+          pa[kb >> 1].h[(kb & 1) * 4 + e] = hb;
+          pl[kb >> 1].h[(kb & 1) * 4 + e] = f2bf(pv - __uint_as_float((uint32_t)hb << 16));
         }
       ls += __shfl_xor(ls, 16, 64);
       ls += __shfl_xor(ls, 32, 64);
@@ -424,6 +430,7 @@ __global__ __launch_bounds__(256) void k_attn_bulk(AttnDesc a) {
           const u32x2_t hi = *(const u32x2_t*)(vr + 16);
           vb.u = u32x4_t{lo.x, lo.y, hi.x, hi.y};
           o[gi][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[j].v, vb.v, o[gi][db], 0, 0, 0);
+          o[gi][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl[j].v, vb.v, o[gi][db], 0, 0, 0);
         }
       }
     }

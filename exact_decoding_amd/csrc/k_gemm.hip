@@ -40,12 +40,16 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// One workgroup: rows [mb*128, mb*128 + 16*MT) x columns [nb*128, nb*128+128)
-// over the K chunks of split `blockIdx.y`, with five waves:
+// One workgroup: rows [mb*128, mb*128 + 16*MT) x the run of (column block,
+// K chunk) units that the split plan deals to workgroup blockIdx.x: n <= nch
+// chunks, the first nA of them chunks cA.. of column block bA, the rest
+// chunks 0.. of block bA + 1.  Five waves:
 //  * waves 0-3 (consumers) own 32 columns each (two 16-column MFMA tiles) for
 //    all MT row tiles; each keeps PF chunks of its weight rows in flight in
-//    registers and issues no other global load, so its in-order load counter
-//    never makes it wait on anything but the chunk it is about to use;
+//    registers and issues no other global load until its stores at the end,
+//    so its in-order load counter never makes it wait on anything but the
+//    chunk it is about to use.  The weight stream runs on across the block
+//    boundary; there the accumulators of block bA are parked in registers;
 //  * wave 4 (producer) stages the x tile of each chunk into a ring of XR LDS
 //    stages, XR-1 chunks ahead of the consumers, from a 2-deep register ring.
 // One barrier per chunk; the producer writes the stage the consumers left
@@ -68,11 +72,15 @@ __global__ __launch_bounds__(320) void k_gemm_bf16(GemmDesc g) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, q = lane >> 4;
-  const int nb = blockIdx.x, split = blockIdx.y, mb = blockIdx.z;
+  const int wg = blockIdx.x, mb = blockIdx.z;
   const int K = g.K;
-  const int nch = K / KC;
-  const int c0 = (int)((long long)split * nch / g.S);
-  const int c1 = (int)((long long)(split + 1) * nch / g.S);
+  const int nch = g.sp.nch;
+  const int U = g.sp.nblk * nch;
+  const int u0 = (int)((long long)wg * U / g.sp.G);
+  const int u1 = (int)((long long)(wg + 1) * U / g.sp.G);
+  const int n = u1 - u0;
+  const int bA = u0 / nch, cA = u0 - bA * nch;
+  const int nA = min(n, nch - cA);
   const int row0 = mb * 128;
   const int xrows = g.rows - row0;  // valid rows in this row block
 
@@ -91,80 +99,94 @@ __global__ __launch_bounds__(320) void k_gemm_bf16(GemmDesc g) {
       lo[j] = row * 64 + xswz(row, pc) * 8;
     }
     u32x4_t ring[2][NP];
-    auto load = [&](int c, u32x4_t (&dst)[NP]) __attribute__((always_inline)) {
+    // chunk t of the run reads K chunk cA + t of block bA, or t - nA of bA + 1
+    auto load = [&](int t, u32x4_t (&dst)[NP]) __attribute__((always_inline)) {
+      const int kc = t < nA ? cA + t : t - nA;
 #pragma unroll
-      for (int j = 0; j < NP; ++j) dst[j] = *(const u32x4_t*)(xp[j] + (size_t)c * KC);
+      for (int j = 0; j < NP; ++j) dst[j] = *(const u32x4_t*)(xp[j] + (size_t)kc * KC);
     };
-    auto store = [&](int c, const u32x4_t (&src)[NP]) __attribute__((always_inline)) {
-      bf16_t* st = xs + ((c - c0) % XR) * XSTAGE;
+    auto store = [&](int t, const u32x4_t (&src)[NP]) __attribute__((always_inline)) {
+      bf16_t* st = xs + (t % XR) * XSTAGE;
 #pragma unroll
       for (int j = 0; j < NP; ++j) *(u32x4_t*)(st + lo[j]) = src[j];
     };
-    // prologue: stages for chunks c0 .. c0+XR-2, ring for the next two
-    for (int c = c0; c < c1 && c < c0 + XR - 1; ++c) {
-      load(c, ring[0]);
-      store(c, ring[0]);
+    // prologue: stages for chunks 0 .. XR-2, ring for the next two
+    for (int t = 0; t < n && t < XR - 1; ++t) {
+      load(t, ring[0]);
+      store(t, ring[0]);
     }
-    load(min(c0 + XR - 1, c1 - 1), ring[(XR - 1) & 1]);
-    load(min(c0 + XR, c1 - 1), ring[XR & 1]);
-    int c = c0;
-    // steady state: store chunk c+XR-1, load chunk c+XR+1 (same ring slot)
-    for (; c + XR + 3 <= c1; c += 2) {
+    load(min(XR - 1, n - 1), ring[(XR - 1) & 1]);
+    load(min(XR, n - 1), ring[XR & 1]);
+    int t = 0;
+    // steady state: store chunk t+XR-1, load chunk t+XR+1 (same ring slot)
+    for (; t + XR + 3 <= n; t += 2) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         lds_barrier();
         const int slot = (XR - 1 + u) & 1;
-        store(c + u + XR - 1, ring[slot]);
-        load(c + u + XR + 1, ring[slot]);
+        store(t + u + XR - 1, ring[slot]);
+        load(t + u + XR + 1, ring[slot]);
       }
     }
-    for (; c < c1; ++c) {
+    for (; t < n; ++t) {
       lds_barrier();
-      const int slot = (c - c0 + XR - 1) & 1;
-      if (c + XR - 1 < c1) {
-        if (slot == 0) store(c + XR - 1, ring[0]); else store(c + XR - 1, ring[1]);
+      const int slot = (t + XR - 1) & 1;
+      if (t + XR - 1 < n) {
+        if (slot == 0) store(t + XR - 1, ring[0]); else store(t + XR - 1, ring[1]);
       }
-      if (c + XR + 1 < c1) {
-        if (slot == 0) load(c + XR + 1, ring[0]); else load(c + XR + 1, ring[1]);
+      if (t + XR + 1 < n) {
+        if (slot == 0) load(t + XR + 1, ring[0]); else load(t + XR + 1, ring[1]);
       }
     }
     return;
   }
 
   // ---------------- consumers: weights + MFMA ----------------
-  const int col0 = nb * NWG;
-  int si = 0, sbase = 0;
-  while (si < g.nseg - 1 && col0 >= sbase + g.seg[si].n) { sbase += g.seg[si].n; ++si; }
-  const bf16_t* W = (const bf16_t*)g.seg[si].w;
-  const int segn = g.seg[si].n;
-  const int nl = col0 - sbase + wave * 32;  // first local weight row of this wave
-
-  // a column past the segment reads row 0; its output is discarded at the
-  // store.  Unpredicated loads let the compiler count outstanding loads
-  // exactly instead of draining them at branch joins.
-  // packed stripes: stripe of 16 rows, K/64 blocks of 2 KB, 1 KB per MFMA
-  // step; a stripe past the segment reads stripe 0 (its output is discarded)
-  const bf16_t* wrow[2];
+  // this wave's columns of column block b: matrix segment, its first column,
+  // and the packed stripe pointers of its two 16-column tiles.  A stripe past
+  // the segment reads stripe 0 (its output is discarded at the store):
+  // unpredicated loads let the compiler count outstanding loads exactly
+  // instead of draining them at branch joins.
+  auto setup = [&](int b, const bf16_t* (&wrow)[2], int& sbase, int& segn, int& nl)
+      __attribute__((always_inline)) {
+    const int col0 = b * NWG;
+    int si = 0;
+    sbase = 0;
+    while (si < g.nseg - 1 && col0 >= sbase + g.seg[si].n) { sbase += g.seg[si].n; ++si; }
+    const bf16_t* W = (const bf16_t*)g.seg[si].w;
+    segn = g.seg[si].n;
+    nl = col0 - sbase + wave * 32;
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int stripe = (nl + t * 16) >> 4;
-    const int ok = nl + t * 16 < segn;
-    wrow[t] = W + (size_t)(ok ? stripe : 0) * nch * 1024 + lane * 8;
-  }
+    for (int t = 0; t < 2; ++t) {
+      const int stripe = (nl + t * 16) >> 4;
+      const int ok = nl + t * 16 < segn;
+      wrow[t] = W + (size_t)(ok ? stripe : 0) * nch * 1024 + lane * 8;
+    }
+  };
+  const bf16_t* wA[2];
+  const bf16_t* wB[2];
+  int sbA, segnA, nlA, sbB = 0, segnB = 0, nlB = 0;
+  setup(bA, wA, sbA, segnA, nlA);
+  if (n > nA) setup(bA + 1, wB, sbB, segnB, nlB);
+  else { wB[0] = wA[0]; wB[1] = wA[1]; }
+  // weight rows of run chunk t, offset by the chunk's K position
+  auto wptr = [&](int t, int tt) __attribute__((always_inline)) {
+    return t < nA ? wA[tt] + (size_t)(cA + t) * 1024 : wB[tt] + (size_t)(t - nA) * 1024;
+  };
 
-  f32x4_t acc[MT][2];
+  f32x4_t acc[MT][2], accA[MT][2];
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
     for (int t = 0; t < 2; ++t) acc[i][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   u32x4_t wr[PF][2][2];
-  auto load_w = [&](int c, u32x4_t (&dst)[2][2]) __attribute__((always_inline)) {
+  auto load_w = [&](int t, u32x4_t (&dst)[2][2]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const bf16_t* p = wrow[t] + (size_t)c * 1024;
-      dst[t][0] = *(const u32x4_t*)p;
-      dst[t][1] = *(const u32x4_t*)(p + 512);
+    for (int tt = 0; tt < 2; ++tt) {
+      const bf16_t* p = wptr(t, tt);
+      dst[tt][0] = *(const u32x4_t*)p;
+      dst[tt][1] = *(const u32x4_t*)(p + 512);
     }
   };
   // A-fragment offsets (bf16) in a stage: row i*16 + r, k 32j + 8q .. +8
@@ -175,9 +197,19 @@ __global__ __launch_bounds__(320) void k_gemm_bf16(GemmDesc g) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) aoff[i][j] = (i * 16 + r) * 64 + xswz(i * 16 + r, 4 * j + q) * 8;
 
-  auto chunk = [&](int c, u32x4_t (&w)[2][2], bool more_w) __attribute__((always_inline)) {
+  auto chunk = [&](int t, u32x4_t (&w)[2][2], bool more_w) __attribute__((always_inline)) {
+    if (t == nA) {
+      // first chunk of block bA + 1: park block bA's sums
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          accA[i][tt] = acc[i][tt];
+          acc[i][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+    }
     lds_barrier();
-    const bf16_t* st = xs + ((c - c0) % XR) * XSTAGE;
+    const bf16_t* st = xs + (t % XR) * XSTAGE;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       U4B b0, b1;
@@ -191,41 +223,53 @@ __global__ __launch_bounds__(320) void k_gemm_bf16(GemmDesc g) {
         acc[i][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b1.v, acc[i][1], 0, 0, 0);
       }
     }
-    if (more_w) load_w(c + PF, w);
+    if (more_w) load_w(t + PF, w);
   };
 
-  // prologue: unconditional (a stage past the split reloads the last chunk
-  // and is never used), so the loop sees a fixed count of loads in flight
+  // prologue: unconditional (a chunk past the run reloads the last one and
+  // is never used), so the loop sees a fixed count of loads in flight
 #pragma unroll
-  for (int s = 0; s < PF; ++s) load_w(min(c0 + s, c1 - 1), wr[s]);
-  int cb = c0;
-  for (; cb + 2 * PF <= c1; cb += PF) {
+  for (int s = 0; s < PF; ++s) load_w(min(s, n - 1), wr[s]);
+  int tb = 0;
+  for (; tb + 2 * PF <= n; tb += PF) {
 #pragma unroll
-    for (int s = 0; s < PF; ++s) chunk(cb + s, wr[s], true);
+    for (int s = 0; s < PF; ++s) chunk(tb + s, wr[s], true);
   }
-  for (; cb < c1; cb += PF) {
+  for (; tb < n; tb += PF) {
 #pragma unroll
     for (int s = 0; s < PF; ++s) {
-      const int c = cb + s;
-      if (c < c1) chunk(c, wr[s], c + PF < c1);
+      const int t = tb + s;
+      if (t < n) chunk(t, wr[s], t + PF < n);
     }
   }
 
-  // D layout of 16x16 MFMA: lane holds rows 4q..4q+3 of column r
-  float* out = g.part + (size_t)split * g.rows_pad * g.N;
+  // D layout of 16x16 MFMA: lane holds rows 4q..4q+3 of column r.  Block bA's
+  // piece goes to its slot among the block's pieces; block bA + 1 starts
+  // with this run, so its piece is slot 0.
+  auto store_block = [&](const f32x4_t (&a)[MT][2], int slot, int sbase, int segn, int nl)
+      __attribute__((always_inline)) {
+    float* out = g.part + (size_t)slot * g.rows_pad * g.N;
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int nloc = nl + t * 16 + r;
-    if (nloc >= segn) continue;
-    const int col = sbase + nloc;
+    for (int tt = 0; tt < 2; ++tt) {
+      const int nloc = nl + tt * 16 + r;
+      if (nloc >= segn) continue;
+      const int col = sbase + nloc;
 #pragma unroll
-    for (int i = 0; i < MT; ++i) {
+      for (int i = 0; i < MT; ++i) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = row0 + i * 16 + q * 4 + e;
-        if (row < g.rows) out[(size_t)row * g.N + col] = acc[i][t][e];
+        for (int e = 0; e < 4; ++e) {
+          const int row = row0 + i * 16 + q * 4 + e;
+          if (row < g.rows) out[(size_t)row * g.N + col] = a[i][tt][e];
+        }
       }
     }
+  };
+  const int slotA = wg - plan_first_wg(g.sp, bA);
+  if (n > nA) {
+    store_block(accA, slotA, sbA, segnA, nlA);
+    store_block(acc, 0, sbB, segnB, nlB);
+  } else {
+    store_block(acc, slotA, sbA, segnA, nlA);
   }
 }
 
@@ -243,29 +287,30 @@ __global__ __launch_bounds__(64) void k_gemm_f32(GemmDesc g) {
   g.part[(size_t)m * g.N + n] = acc;
 }
 
-// Sum of the split partials of one output element, splits in order.  S is a
-// compile-time constant so the S loads are issued together.
-template <int S>
-__device__ __forceinline__ float sum_splits(const float* __restrict__ part, int rows_pad, int N,
-                                            int m, int col) {
-  float p[S];
+// Sum of the pieces of one output element, in K order.  NP is a
+// compile-time bound (>= the plan's np) so the loads are issued together.
+template <int NP>
+__device__ __forceinline__ float sum_pieces(const float* __restrict__ part, const SplitPlan& sp,
+                                            int rows_pad, int N, int m, int col) {
+  if (NP == 1) return part[(size_t)m * N + col];
+  const int np = plan_pieces(sp, col / NWG);
+  float p[NP];
 #pragma unroll
-  for (int s = 0; s < S; ++s) p[s] = part[((size_t)s * rows_pad + m) * N + col];
+  for (int s = 0; s < NP; ++s) p[s] = s < np ? part[((size_t)s * rows_pad + m) * N + col] : 0.f;
   float v = p[0];
 #pragma unroll
-  for (int s = 1; s < S; ++s) v += p[s];
+  for (int s = 1; s < NP; ++s)
+    if (s < np) v += p[s];
   return v;
 }
 
-#define LA_SPLIT_DISPATCH(S_, CALL) \
-  switch (S_) {                     \
-    case 1: CALL(1); break;         \
-    case 2: CALL(2); break;         \
-    case 4: CALL(4); break;         \
-    case 8: CALL(8); break;         \
-    case 16: CALL(16); break;       \
-    default: return hipErrorInvalidValue; \
-  }
+#define LA_SPLIT_DISPATCH(NP_, CALL)          \
+  if ((NP_) <= 1) { CALL(1); }                \
+  else if ((NP_) <= 2) { CALL(2); }           \
+  else if ((NP_) <= 4) { CALL(4); }           \
+  else if ((NP_) <= 8) { CALL(8); }           \
+  else if ((NP_) <= 16) { CALL(16); }         \
+  else return hipErrorInvalidValue;
 
 // Sum the K splits of the fused QKV product, rotate q and k (RoPE at the
 // row's position, pairs (i, i + hd/2)) and store q, k, v.  One thread per
@@ -282,8 +327,8 @@ __global__ __launch_bounds__(256) void k_qkv_epi(QkvEpi e) {
   if (u < npair) {
     const int hh = u / half, i = u - hh * half;
     const int col = hh * hd + i;
-    const float x1 = sum_splits<S>(e.part, e.rows_pad, e.N, m, col);
-    const float x2 = sum_splits<S>(e.part, e.rows_pad, e.N, m, col + half);
+    const float x1 = sum_pieces<S>(e.part, e.sp, e.rows_pad, e.N, m, col);
+    const float x2 = sum_pieces<S>(e.part, e.sp, e.rows_pad, e.N, m, col + half);
     const float2 cs = e.rope[(size_t)pos * half + i];
     const float y1 = x1 * cs.x - x2 * cs.y;
     const float y2 = x1 * cs.y + x2 * cs.x;
@@ -301,22 +346,13 @@ __global__ __launch_bounds__(256) void k_qkv_epi(QkvEpi e) {
     }
   } else {
     const int vi = u - npair;
-    const float v = sum_splits<S>(e.part, e.rows_pad, e.N, m, nq + nk + vi);
+    const float v = sum_pieces<S>(e.part, e.sp, e.rows_pad, e.N, m, nq + nk + vi);
     const int kvh = vi / hd, i = vi - kvh * hd;
     T* vd = (T*)e.vdst;
     T* dst = e.dest == QKV_TO_BLOCK ? vd + (size_t)m * nk + vi
                                     : vd + ((size_t)kvh * e.ld_ctx + pos) * hd + i;
     st_f(dst, v);
   }
-}
-
-template <int S>
-__global__ __launch_bounds__(256) void k_resid_epi(const float* part, int rows_pad, int N,
-                                                   float* x) {
-  const int m = blockIdx.y;
-  const int n = blockIdx.x * 256 + threadIdx.x;
-  if (n >= N) return;
-  x[(size_t)m * N + n] += sum_splits<S>(part, rows_pad, N, m, n);
 }
 
 // x[m] += sum of the split partials; then h[m] = x[m] / sqrt(mean(x^2) + eps) * g
@@ -328,7 +364,8 @@ __global__ __launch_bounds__(256) void k_resid_epi(const float* part, int rows_p
 // t + j*blockDim; the sum of squares is reduced in a fixed order (within a
 // wave by xor-shuffles, then across waves in wave order).
 template <typename T, int S, int NC>
-__global__ __launch_bounds__(1024) void k_resid_norm(const float* __restrict__ part, int rows_pad,
+__global__ __launch_bounds__(1024) void k_resid_norm(const float* __restrict__ part, SplitPlan sp,
+                                                     int rows_pad,
                                                      int d, float* __restrict__ x,
                                                      const T* __restrict__ g, T* __restrict__ h,
                                                      float eps) {
@@ -337,7 +374,7 @@ __global__ __launch_bounds__(1024) void k_resid_norm(const float* __restrict__ p
   float* xr = x + (size_t)m * d;
   float v[NC];
 #pragma unroll
-  for (int j = 0; j < NC; ++j) v[j] = sum_splits<S>(part, rows_pad, d, m, tid + j * nt);
+  for (int j = 0; j < NC; ++j) v[j] = sum_pieces<S>(part, sp, rows_pad, d, m, tid + j * nt);
   float ss = 0.f;
 #pragma unroll
   for (int j = 0; j < NC; ++j) {
@@ -358,22 +395,22 @@ __global__ __launch_bounds__(1024) void k_resid_norm(const float* __restrict__ p
 }
 
 template <int S>
-__global__ __launch_bounds__(256) void k_sum_epi(const float* part, int rows_pad, int N,
-                                                 float* y) {
+__global__ __launch_bounds__(256) void k_sum_epi(const float* part, SplitPlan sp, int rows_pad,
+                                                 int N, float* y) {
   const int m = blockIdx.y;
   const int n = blockIdx.x * 256 + threadIdx.x;
   if (n >= N) return;
-  y[(size_t)m * N + n] = sum_splits<S>(part, rows_pad, N, m, n);
+  y[(size_t)m * N + n] = sum_pieces<S>(part, sp, rows_pad, N, m, n);
 }
 
 template <typename T, int S>
-__global__ __launch_bounds__(256) void k_silu_epi(const float* part, int rows_pad, int F,
-                                                  T* act) {
+__global__ __launch_bounds__(256) void k_silu_epi(const float* part, SplitPlan sp, int rows_pad,
+                                                  int F, T* act) {
   const int m = blockIdx.y;
   const int f = blockIdx.x * 256 + threadIdx.x;
   if (f >= F) return;
-  const float gt = sum_splits<S>(part, rows_pad, 2 * F, m, f);
-  const float up = sum_splits<S>(part, rows_pad, 2 * F, m, F + f);
+  const float gt = sum_pieces<S>(part, sp, rows_pad, 2 * F, m, f);
+  const float up = sum_pieces<S>(part, sp, rows_pad, 2 * F, m, F + f);
   const float sg = gt / (1.0f + expf(-gt));
   st_f(act + (size_t)m * F + f, sg * up);
 }
@@ -401,15 +438,39 @@ hipError_t launch_pack(const void* src, int N, int K, void* dst, hipStream_t st)
   return hipGetLastError();
 }
 
-int gemm_splits(int N, int K, int dtype) {
-  if (dtype != LA_BF16) return 1;
-  const int nblk = (N + NWG - 1) / NWG;
-  const int nch = K / KC;
-  int S = 1;
-  // the largest power-of-two split that keeps the grid within one round of
-  // LA_GEMM_TARGET_WG workgroups (one per CU), with >= 4 chunks per split
-  while (nblk * S * 2 <= LA_GEMM_TARGET_WG && (S * 2) * 4 <= nch && S < 16) S *= 2;
-  return S;
+SplitPlan gemm_plan_whole(int N, int K) {
+  SplitPlan p{};
+  p.nch = K / KC;
+  p.nblk = (N + NWG - 1) / NWG;
+  p.G = p.nblk;
+  p.np = 1;
+  return p;
+}
+
+SplitPlan gemm_plan(int N, int K, int dtype) {
+  SplitPlan p = gemm_plan_whole(N, K);
+  if (dtype != LA_BF16 || p.nch < 1) return p;
+  // Workgroups: whole column blocks when they already fill >= 90% of the
+  // rounds of LA_GEMM_TARGET_WG workgroups (one per CU); otherwise deal the
+  // units out to full rounds, keeping >= 4 chunks per workgroup, <= 15
+  // pieces per block on average, and >= nblk workgroups (so a run spans at
+  // most two column blocks).
+  const int T = LA_GEMM_TARGET_WG;
+  const int rounds = (p.nblk + T - 1) / T;
+  const long long U = (long long)p.nblk * p.nch;
+  if (p.nblk * 10 < rounds * T * 9) {
+    long long G = (long long)rounds * T;
+    if (G > U / 4) G = U / 4;
+    if (G > 15LL * p.nblk) G = 15LL * p.nblk;
+    if (G < p.nblk) G = p.nblk;
+    // plan_wg_of works in 32-bit unsigned arithmetic
+    if (U * G < (1LL << 31)) p.G = (int)G;
+  }
+  for (int b = 0; b < p.nblk; ++b) {
+    const int k = plan_pieces(p, b);
+    if (k > p.np) p.np = k;
+  }
+  return p;
 }
 
 hipError_t launch_gemm(const GemmDesc& g, int dtype, hipStream_t st) {
@@ -418,13 +479,13 @@ hipError_t launch_gemm(const GemmDesc& g, int dtype, hipStream_t st) {
     hipLaunchKernelGGL(k_gemm_f32, grid, dim3(64), 0, st, g);
     return hipGetLastError();
   }
-  const int nblk = (g.N + NWG - 1) / NWG;
+  if (g.sp.nblk != (g.N + NWG - 1) / NWG || g.sp.nch != g.K / KC) return hipErrorInvalidValue;
   const int mblk = (g.rows + 127) / 128;
   const int rows_last = g.rows - (mblk - 1) * 128;
   // the row-tile count only changes how many rows one workgroup carries, not
   // the arithmetic of any row
   const int mt = mblk > 1 ? 8 : (rows_last + 15) / 16;
-  dim3 grid(nblk, g.S, mblk);
+  dim3 grid(g.sp.G, 1, mblk);
   const dim3 blk(320);
   switch (mt) {
     case 1: hipLaunchKernelGGL(k_gemm_bf16<1>, grid, blk, 0, st, g); break;
@@ -447,17 +508,8 @@ hipError_t launch_qkv_epi(const QkvEpi& e, int dtype, hipStream_t st) {
     hipLaunchKernelGGL((k_qkv_epi<bf16_t, S_>), grid, dim3(256), 0, st, e);     \
   else                                                                          \
     hipLaunchKernelGGL((k_qkv_epi<float, S_>), grid, dim3(256), 0, st, e);
-  LA_SPLIT_DISPATCH(e.S, LA_QKV)
+  LA_SPLIT_DISPATCH(e.sp.np, LA_QKV)
 #undef LA_QKV
-  return hipGetLastError();
-}
-
-hipError_t launch_resid_epi(const float* part, int S, int rows_pad, int N, int rows, float* x,
-                            hipStream_t st) {
-#define LA_RE(S_) \
-  hipLaunchKernelGGL((k_resid_epi<S_>), dim3((N + 255) / 256, rows), dim3(256), 0, st, part, rows_pad, N, x);
-  LA_SPLIT_DISPATCH(S, LA_RE)
-#undef LA_RE
   return hipGetLastError();
 }
 
@@ -468,18 +520,19 @@ static int norm_nc(int d) {
   return 0;
 }
 
-hipError_t launch_resid_norm(const float* part, int S, int rows_pad, int d, int rows, float* x,
-                             const void* g, void* h, float eps, int dtype, hipStream_t st) {
+hipError_t launch_resid_norm(const float* part, const SplitPlan& sp, int rows_pad, int d,
+                             int rows, float* x, const void* g, void* h, float eps, int dtype,
+                             hipStream_t st) {
   const int nc = norm_nc(d);
   if (!nc) return hipErrorInvalidValue;
   const dim3 blk(d / nc);
 #define LA_RN2(S_, NC_)                                                                        \
   if (dtype == LA_BF16)                                                                        \
-    hipLaunchKernelGGL((k_resid_norm<bf16_t, S_, NC_>), dim3(rows), blk, 0, st, part, rows_pad, \
-                       d, x, (const bf16_t*)g, (bf16_t*)h, eps);                               \
+    hipLaunchKernelGGL((k_resid_norm<bf16_t, S_, NC_>), dim3(rows), blk, 0, st, part, sp,      \
+                       rows_pad, d, x, (const bf16_t*)g, (bf16_t*)h, eps);                     \
   else                                                                                         \
-    hipLaunchKernelGGL((k_resid_norm<float, S_, NC_>), dim3(rows), blk, 0, st, part, rows_pad,  \
-                       d, x, (const float*)g, (float*)h, eps);
+    hipLaunchKernelGGL((k_resid_norm<float, S_, NC_>), dim3(rows), blk, 0, st, part, sp,       \
+                       rows_pad, d, x, (const float*)g, (float*)h, eps);
 #define LA_RN(S_)                                                       \
   switch (nc) {                                                         \
     case 1: LA_RN2(S_, 1) break;                                        \
@@ -490,31 +543,32 @@ hipError_t launch_resid_norm(const float* part, int S, int rows_pad, int d, int 
     case 16: LA_RN2(S_, 16) break;                                      \
     default: return hipErrorInvalidValue;                               \
   }
-  LA_SPLIT_DISPATCH(S, LA_RN)
+  LA_SPLIT_DISPATCH(sp.np, LA_RN)
 #undef LA_RN
 #undef LA_RN2
   return hipGetLastError();
 }
 
-hipError_t launch_sum_epi(const float* part, int S, int rows_pad, int N, int rows, float* y,
-                          hipStream_t st) {
-#define LA_SE(S_) \
-  hipLaunchKernelGGL((k_sum_epi<S_>), dim3((N + 255) / 256, rows), dim3(256), 0, st, part, rows_pad, N, y);
-  LA_SPLIT_DISPATCH(S, LA_SE)
+hipError_t launch_sum_epi(const float* part, const SplitPlan& sp, int rows_pad, int N, int rows,
+                          float* y, hipStream_t st) {
+#define LA_SE(S_)                                                                           \
+  hipLaunchKernelGGL((k_sum_epi<S_>), dim3((N + 255) / 256, rows), dim3(256), 0, st, part, sp, \
+                     rows_pad, N, y);
+  LA_SPLIT_DISPATCH(sp.np, LA_SE)
 #undef LA_SE
   return hipGetLastError();
 }
 
-hipError_t launch_silu_epi(const float* part, int S, int rows_pad, int F, int rows, void* act,
-                           int dtype, hipStream_t st) {
+hipError_t launch_silu_epi(const float* part, const SplitPlan& sp, int rows_pad, int F, int rows,
+                           void* act, int dtype, hipStream_t st) {
 #define LA_SI(S_)                                                                              \
   if (dtype == LA_BF16)                                                                        \
     hipLaunchKernelGGL((k_silu_epi<bf16_t, S_>), dim3((F + 255) / 256, rows), dim3(256), 0, st, \
-                       part, rows_pad, F, (bf16_t*)act);                                       \
+                       part, sp, rows_pad, F, (bf16_t*)act);                                   \
   else                                                                                         \
     hipLaunchKernelGGL((k_silu_epi<float, S_>), dim3((F + 255) / 256, rows), dim3(256), 0, st,  \
-                       part, rows_pad, F, (float*)act);
-  LA_SPLIT_DISPATCH(S, LA_SI)
+                       part, sp, rows_pad, F, (float*)act);
+  LA_SPLIT_DISPATCH(sp.np, LA_SI)
 #undef LA_SI
   return hipGetLastError();
 }

@@ -82,7 +82,8 @@ struct Shape {
   int L, d, H, Hkv, hd, F, V, dt;
   int M, rows_cap, ld_ctx;
   int N, W, G, cap;
-  int S_qkv, S_o, S_gu, S_d;
+  SplitPlan sp_qkv, sp_o, sp_gu, sp_d, sp_lm;
+  double pc_qkv, pc_o, pc_gu, pc_d;  // mean pieces per column block (profile bytes)
   int att_chunk, att_nsplit;  // MFMA-attention chunking (0 = per-row kernel only)
 };
 
@@ -100,10 +101,21 @@ Shape make_shape(const la_model* m, const la_decode_params* p) {
   s.ld_ctx = p->max_ctx;
   s.rows_cap = s.M > p->max_ctx ? s.M : p->max_ctx;
   const int nqkv = (s.H + 2 * s.Hkv) * s.hd;
-  s.S_qkv = gemm_splits(nqkv, s.d, s.dt);
-  s.S_o = gemm_splits(s.d, s.H * s.hd, s.dt);
-  s.S_gu = gemm_splits(2 * s.F, s.d, s.dt);
-  s.S_d = gemm_splits(s.d, s.F, s.dt);
+  s.sp_qkv = gemm_plan(nqkv, s.d, s.dt);
+  s.sp_o = gemm_plan(s.d, s.H * s.hd, s.dt);
+  s.sp_gu = gemm_plan(2 * s.F, s.d, s.dt);
+  s.sp_d = gemm_plan(s.d, s.F, s.dt);
+  // the LM head writes the logits directly: whole column blocks, one piece
+  s.sp_lm = gemm_plan_whole(s.V, s.d);
+  auto mean_pieces = [](const SplitPlan& p) {
+    double t = 0;
+    for (int b = 0; b < p.nblk; ++b) t += p.np > 1 ? plan_pieces(p, b) : 1;
+    return t / p.nblk;
+  };
+  s.pc_qkv = mean_pieces(s.sp_qkv);
+  s.pc_o = mean_pieces(s.sp_o);
+  s.pc_gu = mean_pieces(s.sp_gu);
+  s.pc_d = mean_pieces(s.sp_d);
   s.att_chunk = attn_chunk(s.ld_ctx, s.dt, s.hd);
   s.att_nsplit = s.att_chunk ? (s.ld_ctx + s.att_chunk - 1) / s.att_chunk : 0;
   return s;
@@ -116,14 +128,14 @@ Views plan_views(const Shape& s) {
   const size_t R = (size_t)s.rows_cap;
   const int nqkv = (s.H + 2 * s.Hkv) * s.hd;
   size_t part = 0;
-  auto upd = [&](int S, int N) {
-    const size_t b = (size_t)S * R * N * 4;
+  auto upd = [&](const SplitPlan& sp, int N) {
+    const size_t b = (size_t)sp.np * R * N * 4;
     if (b > part) part = b;
   };
-  upd(s.S_qkv, nqkv);
-  upd(s.S_o, s.d);
-  upd(s.S_gu, 2 * s.F);
-  upd(s.S_d, s.d);
+  upd(s.sp_qkv, nqkv);
+  upd(s.sp_o, s.d);
+  upd(s.sp_gu, 2 * s.F);
+  upd(s.sp_d, s.d);
   v.x = w.take(R * s.d * 4);
   v.h = w.take(R * s.d * es);
   v.q = w.take(R * s.H * s.hd * es);
@@ -201,6 +213,9 @@ struct la_session {
     }
     return evs[ev_next++];
   }
+  // la_step_trace: destination of the per-layer copies, null otherwise
+  char* trace = nullptr;
+  size_t trace_off = 0;
   int P_host = 0;
   double sum_off = 0;  // sum over block rows of (position - P)
   int total = 0;
@@ -250,6 +265,15 @@ hipError_t launch_checked(hipError_t e, const char* what, hipStream_t st) {
     }                                                                             \
   } while (0)
 
+// la_step_trace: append `bytes` from device memory `src` to the trace.
+hipError_t trace_copy(la_session* ss, const void* src, size_t bytes) {
+  if (!ss->trace) return hipSuccess;
+  hipError_t e = hipMemcpyAsync(ss->trace + ss->trace_off, src, bytes, hipMemcpyDeviceToDevice,
+                                ss->stream);
+  ss->trace_off += bytes;
+  return e;
+}
+
 // The decoder forward over `rows` rows whose token ids and positions are on
 // the device.  mode_prefill: K/V are written straight to the cache at each
 // row's position and attention is causal over the cache; otherwise K/V go to
@@ -285,7 +309,11 @@ int enqueue_forward(la_session* ss, int rows, bool mode_prefill) {
         "embed");
   LA_KP(LA_PROF_NORM, R * D * (ES + 4.0), 0,
         launch_rmsnorm(x, m->layers[0].attn_norm, h, rows, s.d, eps, dt, st), "rmsnorm_attn");
+  const size_t xrow = (size_t)rows * s.d * 4, hrow = (size_t)rows * s.d * es;
+  const size_t qrow = (size_t)rows * s.H * s.hd * es;
   for (int l = 0; l < s.L; ++l) {
+    LA_K(trace_copy(ss, x, xrow), "trace");
+    LA_K(trace_copy(ss, h, hrow), "trace");
     const LayerW& w = m->layers[l];
     char* kc = ss->at<char>(ss->v.kc) + (size_t)l * s.Hkv * s.ld_ctx * s.hd * es;
     char* vc = ss->at<char>(ss->v.vc) + (size_t)l * s.Hkv * s.ld_ctx * s.hd * es;
@@ -297,18 +325,19 @@ int enqueue_forward(la_session* ss, int rows, bool mode_prefill) {
     g.seg[0] = {w.wq, s.H * s.hd};
     g.seg[1] = {w.wk, s.Hkv * s.hd};
     g.seg[2] = {w.wv, s.Hkv * s.hd};
-    g.N = nqkv; g.S = s.S_qkv; g.part = part;
+    g.N = nqkv; g.sp = s.sp_qkv; g.part = part;
     LA_KP(LA_PROF_GEMM, gemm_bytes(nqkv, s.d), 2.0 * R * nqkv * s.d, launch_gemm(g, dt, st),
           "gemm_qkv");
     QkvEpi e{};
-    e.part = part; e.S = s.S_qkv; e.rows_pad = rows; e.N = nqkv; e.rows = rows;
+    e.part = part; e.sp = s.sp_qkv; e.rows_pad = rows; e.N = nqkv; e.rows = rows;
     e.H = s.H; e.Hkv = s.Hkv; e.hd = s.hd; e.pos = pos;
     e.rope = ss->at<float2>(ss->v.rope); e.q = q;
     e.kdst = mode_prefill ? (void*)kc : (void*)kb;
     e.vdst = mode_prefill ? (void*)vc : (void*)vb;
     e.dest = mode_prefill ? QKV_TO_CACHE : QKV_TO_BLOCK;
     e.ld_ctx = s.ld_ctx;
-    LA_KP(LA_PROF_EPI, R * nqkv * (4.0 * s.S_qkv + ES), 0, launch_qkv_epi(e, dt, st), "qkv_epi");
+    LA_KP(LA_PROF_EPI, R * nqkv * (4.0 * s.pc_qkv + ES), 0, launch_qkv_epi(e, dt, st), "qkv_epi");
+    LA_K(trace_copy(ss, q, qrow), "trace");
 
     AttnDesc a{};
     a.q = q; a.kc = kc; a.vc = vc; a.kb = kb; a.vb = vb; a.out = att; a.pos = pos;
@@ -327,36 +356,42 @@ int enqueue_forward(la_session* ss, int rows, bool mode_prefill) {
       a.tail_ml = a.tail_o + (size_t)rows * s.H * s.hd;
     }
     LA_KP(LA_PROF_ATTN, att_bytes, att_flops, launch_attention(a, dt, st), "attention");
+    LA_K(trace_copy(ss, att, qrow), "trace");
 
     g = GemmDesc{};
     g.x = att; g.rows = rows; g.rows_pad = rows; g.K = s.H * s.hd; g.nseg = 1;
-    g.seg[0] = {w.wo, s.d}; g.N = s.d; g.S = s.S_o; g.part = part;
+    g.seg[0] = {w.wo, s.d}; g.N = s.d; g.sp = s.sp_o; g.part = part;
     LA_KP(LA_PROF_GEMM, gemm_bytes(s.d, s.H * s.hd), 2.0 * R * s.d * s.H * s.hd,
           launch_gemm(g, dt, st), "gemm_o");
-    LA_KP(LA_PROF_EPI, R * D * (4.0 * s.S_o + 8.0 + ES), 0,
-          launch_resid_norm(part, s.S_o, rows, s.d, rows, x, w.mlp_norm, h, eps, dt, st),
+    LA_KP(LA_PROF_EPI, R * D * (4.0 * s.pc_o + 8.0 + ES), 0,
+          launch_resid_norm(part, s.sp_o, rows, s.d, rows, x, w.mlp_norm, h, eps, dt, st),
           "resid_o_norm");
+    LA_K(trace_copy(ss, x, xrow), "trace");
+    LA_K(trace_copy(ss, h, hrow), "trace");
 
     g = GemmDesc{};
     g.x = h; g.rows = rows; g.rows_pad = rows; g.K = s.d; g.nseg = 2;
     g.seg[0] = {w.wg, s.F}; g.seg[1] = {w.wu, s.F};
-    g.N = 2 * s.F; g.S = s.S_gu; g.part = part;
+    g.N = 2 * s.F; g.sp = s.sp_gu; g.part = part;
     LA_KP(LA_PROF_GEMM, gemm_bytes(2.0 * s.F, s.d), 2.0 * R * 2.0 * s.F * s.d,
           launch_gemm(g, dt, st), "gemm_gate_up");
-    LA_KP(LA_PROF_EPI, R * s.F * (8.0 * s.S_gu + ES), 0,
-          launch_silu_epi(part, s.S_gu, rows, s.F, rows, act, dt, st), "silu_epi");
+    LA_KP(LA_PROF_EPI, R * s.F * (8.0 * s.pc_gu + ES), 0,
+          launch_silu_epi(part, s.sp_gu, rows, s.F, rows, act, dt, st), "silu_epi");
+    LA_K(trace_copy(ss, act, (size_t)rows * s.F * es), "trace");
 
     g = GemmDesc{};
     g.x = act; g.rows = rows; g.rows_pad = rows; g.K = s.F; g.nseg = 1;
-    g.seg[0] = {w.wd, s.d}; g.N = s.d; g.S = s.S_d; g.part = part;
+    g.seg[0] = {w.wd, s.d}; g.N = s.d; g.sp = s.sp_d; g.part = part;
     LA_KP(LA_PROF_GEMM, gemm_bytes(s.d, s.F), 2.0 * R * s.d * s.F, launch_gemm(g, dt, st),
           "gemm_down");
     // the next layer's attention norm, or the final norm after the last layer
     const void* gnext = l + 1 < s.L ? m->layers[l + 1].attn_norm : m->final_norm;
-    LA_KP(LA_PROF_EPI, R * D * (4.0 * s.S_d + 8.0 + ES), 0,
-          launch_resid_norm(part, s.S_d, rows, s.d, rows, x, gnext, h, eps, dt, st),
+    LA_KP(LA_PROF_EPI, R * D * (4.0 * s.pc_d + 8.0 + ES), 0,
+          launch_resid_norm(part, s.sp_d, rows, s.d, rows, x, gnext, h, eps, dt, st),
           "resid_down_norm");
   }
+  LA_K(trace_copy(ss, x, xrow), "trace");
+  LA_K(trace_copy(ss, h, hrow), "trace");
   return LA_OK;
 }
 
@@ -378,17 +413,33 @@ int enqueue_step(la_session* ss) {
 
   const double R = s.M, ES = (double)dtype_size(dt);
   LA_KP(LA_PROF_BOOK, 0, 0, launch_gather(pool, io, ss->lay, st), "gather");
+  const size_t es = dtype_size(dt);
+  const size_t cache_bytes = (size_t)s.L * s.Hkv * s.ld_ctx * s.hd * es;
+  const size_t blk_bytes = (size_t)s.L * s.M * s.Hkv * s.hd * es;
+  if (ss->trace) {
+    int32_t hdr[16] = {ss->P_host, s.M, s.ld_ctx, s.L, s.d, s.H, s.Hkv, s.hd, s.F, s.V, dt};
+    LA_K(hipMemcpyAsync(ss->trace, hdr, sizeof(hdr), hipMemcpyHostToDevice, st), "trace");
+    LA_K(hipStreamSynchronize(st), "trace");  // hdr is a stack array
+    ss->trace_off = sizeof(hdr);
+  }
+  LA_K(trace_copy(ss, io.ids, (size_t)s.M * 4), "trace");
+  LA_K(trace_copy(ss, io.pos, (size_t)s.M * 4), "trace");
+  LA_K(trace_copy(ss, ss->at(ss->v.kc), cache_bytes), "trace");
+  LA_K(trace_copy(ss, ss->at(ss->v.vc), cache_bytes), "trace");
   int rc = enqueue_forward(ss, s.M, false);
   if (rc != LA_OK) return rc;
+  LA_K(trace_copy(ss, ss->at(ss->v.kb), blk_bytes), "trace");
+  LA_K(trace_copy(ss, ss->at(ss->v.vb), blk_bytes), "trace");
   const la_model* m = ss->m;
   float* x = ss->at<float>(ss->v.x);
   void* h = ss->at(ss->v.h);
   GemmDesc g{};
   g.x = h; g.rows = s.M; g.rows_pad = s.M; g.K = s.d; g.nseg = 1;
-  g.seg[0] = {m->lm_head, s.V}; g.N = s.V; g.S = 1;
+  g.seg[0] = {m->lm_head, s.V}; g.N = s.V; g.sp = s.sp_lm;
   g.part = ss->at<float>(ss->v.logits);
   LA_KP(LA_PROF_LMHEAD, ((double)s.V * s.d + R * s.d) * ES + R * s.V * 4.0,
         2.0 * R * s.V * s.d, launch_gemm(g, dt, st), "gemm_lm_head");
+  LA_K(trace_copy(ss, ss->at(ss->v.logits), (size_t)s.M * s.V * 4), "trace");
   LA_KP(LA_PROF_ARGMAX, R * s.V * 4.0, 0,
         launch_argmax(ss->at<float>(ss->v.logits), s.M, s.V, ss->at<int32_t>(ss->v.amax), st),
         "argmax");
@@ -587,8 +638,20 @@ int la_prefill(la_model* m, const la_decode_params* p, const int32_t* prompt, in
   return LA_OK;
 }
 
+static size_t trace_bytes(const Shape& s) {
+  const size_t es = dtype_size(s.dt), M = (size_t)s.M;
+  const size_t xrow = M * s.d * 4, hrow = M * s.d * es, qrow = M * s.H * s.hd * es;
+  size_t b = 16 * 4 + 2 * M * 4;
+  b += 2 * (size_t)s.L * s.Hkv * s.ld_ctx * s.hd * es;
+  b += (size_t)s.L * (2 * xrow + 2 * hrow + 2 * qrow + M * s.F * es);
+  b += xrow + hrow;
+  b += 2 * (size_t)s.L * M * s.Hkv * s.hd * es;
+  b += M * s.V * 4;
+  return b;
+}
+
 static int step_impl(la_session* s, int32_t* out_tokens, int32_t out_cap, int32_t* n_out,
-                     la_profile_t* prof) {
+                     la_profile_t* prof, char* trace = nullptr) {
   if (!s || !out_tokens || !n_out) return fail(LA_EINVAL, "null argument");
   *n_out = 0;
   if (s->poisoned) return fail(LA_ESTATE, "session poisoned by an earlier HIP error");
@@ -603,6 +666,11 @@ static int step_impl(la_session* s, int32_t* out_tokens, int32_t out_cap, int32_
     s->ev_next = 0;
     rc = enqueue_step(s);
     s->prof_on = false;
+  } else if (trace) {
+    s->trace = trace;
+    s->trace_off = 0;
+    rc = enqueue_step(s);
+    s->trace = nullptr;
   } else if (s->exec) {
     hipError_t e = hipGraphLaunch(s->exec, s->stream);
     if (e != hipSuccess) rc = fail(LA_EHIP, std::string("hipGraphLaunch: ") + hipGetErrorString(e));
@@ -652,6 +720,21 @@ int la_step_profile(la_session* s, int32_t* out_tokens, int32_t out_cap, int32_t
                     la_profile_t* prof) {
   if (!prof) return fail(LA_EINVAL, "null prof");
   return step_impl(s, out_tokens, out_cap, n_out, prof);
+}
+
+int la_step_trace_bytes(const la_session* s, size_t* bytes) {
+  if (!s || !bytes) return fail(LA_EINVAL, "null argument");
+  *bytes = trace_bytes(s->s);
+  return LA_OK;
+}
+
+int la_step_trace(la_session* s, int32_t* out_tokens, int32_t out_cap, int32_t* n_out,
+                  void* dev_trace, size_t bytes) {
+  if (!dev_trace) return fail(LA_EINVAL, "null trace buffer");
+  if (!s) return fail(LA_EINVAL, "null session");
+  if (bytes < trace_bytes(s->s))
+    return fail(LA_ENOMEM, "trace buffer too small: need " + std::to_string(trace_bytes(s->s)));
+  return step_impl(s, out_tokens, out_cap, n_out, nullptr, (char*)dev_trace);
 }
 
 int la_pool_stats(const la_session* s, la_pool_stats_t* out) {
@@ -747,8 +830,8 @@ int la_pack_weight(const void* src, int32_t N, int32_t K, void* dst, void* hip_s
 
 size_t la_kernel_gemm_ws_bytes(int32_t M, int32_t K, int32_t N) {
   if (M < 1 || K < 1 || N < 1) return 0;
-  const int S = gemm_splits(N, K, LA_BF16);
-  return S > 1 ? (size_t)S * M * N * 4 : 0;
+  const SplitPlan sp = gemm_plan(N, K, LA_BF16);
+  return sp.np > 1 ? (size_t)sp.np * M * N * 4 : 0;
 }
 
 int la_kernel_gemm(const void* x, int32_t M, int32_t K, const void* w, int32_t N, float* y,
@@ -757,15 +840,15 @@ int la_kernel_gemm(const void* x, int32_t M, int32_t K, const void* w, int32_t N
   if (M < 1 || K < 1 || N < 1) return fail(LA_EINVAL, "sizes must be >= 1");
   if (dtype != LA_F32 && dtype != LA_BF16) return fail(LA_EINVAL, "bad dtype");
   if (dtype == LA_BF16 && K % 64) return fail(LA_EINVAL, "bf16 needs K % 64 == 0");
-  const int S = gemm_splits(N, K, dtype);
-  const size_t need = S > 1 ? (size_t)S * M * N * 4 : 0;
+  const SplitPlan sp = gemm_plan(N, K, dtype);
+  const size_t need = sp.np > 1 ? (size_t)sp.np * M * N * 4 : 0;
   if (ws_bytes < need || (need && !ws)) return fail(LA_ENOMEM, "workspace too small");
   hipStream_t st = (hipStream_t)hip_stream;
   GemmDesc g{};
   g.x = x; g.rows = M; g.rows_pad = M; g.K = K; g.nseg = 1; g.seg[0] = {w, N};
-  g.N = N; g.S = S; g.part = S > 1 ? (float*)ws : y;
+  g.N = N; g.sp = sp; g.part = sp.np > 1 ? (float*)ws : y;
   LA_HIP(launch_gemm(g, dtype, st));
-  if (S > 1) LA_HIP(launch_sum_epi((float*)ws, S, M, N, M, y, st));
+  if (sp.np > 1) LA_HIP(launch_sum_epi((float*)ws, sp, M, N, M, y, st));
   return LA_OK;
 }
 

@@ -58,8 +58,33 @@ struct RowLayout {
 };
 
 // ---------------------------------------------------------------------------
-// GEMM: y_part[s][m][n] = sum over split s of x[m][k] * w[n][k]
+// GEMM: y_part[p][m][n] = sum over the K range of piece p of x[m][k] * w[n][k]
 // ---------------------------------------------------------------------------
+// How one product's work is dealt out.  Its units are (column block of 128,
+// K chunk of 64) pairs in block-major order, U = nblk * nch of them; workgroup
+// w takes units [floor(w U / G), floor((w+1) U / G)), at most nch of them, so
+// it covers the tail of one column block and possibly the head of the next.
+// The pieces a column block is cut into are summed in K order by the
+// epilogue.  The plan depends on (N, K) only, never on the row count, so a
+// row gets the same sums at any M.
+struct SplitPlan {
+  int nch;   // K / 64
+  int nblk;  // column blocks of 128
+  int G;     // workgroups per 128-row block
+  int np;    // most pieces any column block is cut into (1: no partial sums)
+};
+
+// workgroup holding unit u, and the pieces of column block b
+__host__ __device__ inline int plan_wg_of(const SplitPlan& p, int u) {
+  return (int)(((unsigned)(u + 1) * (unsigned)p.G - 1u) / (unsigned)(p.nblk * p.nch));
+}
+__host__ __device__ inline int plan_first_wg(const SplitPlan& p, int b) {
+  return plan_wg_of(p, b * p.nch);
+}
+__host__ __device__ inline int plan_pieces(const SplitPlan& p, int b) {
+  return plan_wg_of(p, (b + 1) * p.nch - 1) - plan_first_wg(p, b) + 1;
+}
+
 struct GemmSeg {
   const void* w;  // [n][K] row-major
   int n;          // rows of this segment
@@ -72,12 +97,13 @@ struct GemmDesc {
   int nseg;
   GemmSeg seg[3];
   int N;          // total columns (sum of segment rows)
-  int S;          // K splits
-  float* part;    // [S][rows_pad][N]
+  SplitPlan sp;   // how the (column block, K chunk) units are dealt out
+  float* part;    // [sp.np][rows_pad][N]; the output itself when sp.np == 1
   int rows_pad;   // leading row count of part
 };
 
-int gemm_splits(int N, int K, int dtype);
+SplitPlan gemm_plan(int N, int K, int dtype);
+SplitPlan gemm_plan_whole(int N, int K);  // one workgroup per column block
 size_t packed_bytes(int N, int K);
 hipError_t launch_pack(const void* src, int N, int K, void* dst, hipStream_t st);
 hipError_t launch_gemm(const GemmDesc& g, int dtype, hipStream_t st);
@@ -85,7 +111,7 @@ hipError_t launch_gemm(const GemmDesc& g, int dtype, hipStream_t st);
 // epilogues of the split GEMM
 enum QkvDest { QKV_TO_BLOCK = 0, QKV_TO_CACHE = 1 };
 struct QkvEpi {
-  const float* part; int S; int rows_pad; int N;
+  const float* part; SplitPlan sp; int rows_pad; int N;
   int rows, H, Hkv, hd;
   const int32_t* pos;      // absolute position of each row
   const float2* rope;      // [max_ctx][hd/2] (cos, sin)
@@ -94,14 +120,13 @@ struct QkvEpi {
   int dest; int ld_ctx;
 };
 hipError_t launch_qkv_epi(const QkvEpi& e, int dtype, hipStream_t st);
-hipError_t launch_resid_epi(const float* part, int S, int rows_pad, int N, int rows, float* x,
-                            hipStream_t st);
-hipError_t launch_resid_norm(const float* part, int S, int rows_pad, int d, int rows, float* x,
-                             const void* g, void* h, float eps, int dtype, hipStream_t st);
-hipError_t launch_silu_epi(const float* part, int S, int rows_pad, int F, int rows, void* act,
-                           int dtype, hipStream_t st);
-hipError_t launch_sum_epi(const float* part, int S, int rows_pad, int N, int rows, float* y,
-                          hipStream_t st);
+hipError_t launch_resid_norm(const float* part, const SplitPlan& sp, int rows_pad, int d,
+                             int rows, float* x, const void* g, void* h, float eps, int dtype,
+                             hipStream_t st);
+hipError_t launch_silu_epi(const float* part, const SplitPlan& sp, int rows_pad, int F, int rows,
+                           void* act, int dtype, hipStream_t st);
+hipError_t launch_sum_epi(const float* part, const SplitPlan& sp, int rows_pad, int N, int rows,
+                          float* y, hipStream_t st);
 
 // norm / embedding / argmax
 hipError_t launch_rmsnorm(const float* x, const void* g, void* y, int rows, int d, float eps,

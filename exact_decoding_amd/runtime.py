@@ -110,6 +110,50 @@ class Session:
         self.done = rc == B.LA_DONE
         return toks, prof
 
+    def step_trace(self) -> tuple[list[int], dict]:
+        """One step with every forward intermediate copied out (la_step_trace).
+        Returns the step's tokens and a dict of host arrays: 16-bit model
+        tensors as uint16 bit patterns, float32 tensors as float32."""
+        torch = _torch()
+        nbytes = B.la_step_trace_bytes(self.handle)
+        buf = torch.empty(nbytes, dtype=torch.uint8, device=self.model.device)
+        rc, toks = B.la_step_trace(self.handle, max(self.params.N, 1), buf, nbytes)
+        self.tokens.extend(toks)
+        if toks:
+            self.per_step.append(len(toks))
+        self.done = rc == B.LA_DONE
+        raw = buf.cpu().numpy()
+        del buf
+        hdr = raw[:64].view(np.int32)
+        P, M, ctx, L, d, H, Hkv, hd, F, V, dt = (int(v) for v in hdr[:11])
+        edt = np.uint16 if dt == B.LA_BF16 else np.float32
+        off = 64
+
+        def take(dtype, shape):
+            nonlocal off
+            n = int(np.prod(shape)) * np.dtype(dtype).itemsize
+            a = raw[off:off + n].view(dtype).reshape(shape)
+            off += n
+            return a
+
+        t = {"P": P, "M": M, "ids": take(np.int32, (M,)), "pos": take(np.int32, (M,))}
+        t["kc"] = take(edt, (L, Hkv, ctx, hd))
+        t["vc"] = take(edt, (L, Hkv, ctx, hd))
+        t["layers"] = []
+        for _ in range(L):
+            t["layers"].append({
+                "x_in": take(np.float32, (M, d)), "h1": take(edt, (M, d)),
+                "q": take(edt, (M, H * hd)), "attn": take(edt, (M, H * hd)),
+                "x_mid": take(np.float32, (M, d)), "h2": take(edt, (M, d)),
+                "act": take(edt, (M, F))})
+        t["x_final"] = take(np.float32, (M, d))
+        t["h_final"] = take(edt, (M, d))
+        t["kb"] = take(edt, (L, M, Hkv, hd))
+        t["vb"] = take(edt, (L, M, Hkv, hd))
+        t["logits"] = take(np.float32, (M, V))
+        assert off == nbytes, (off, nbytes)
+        return toks, t
+
     def decode(self) -> list[int]:
         while not self.done:
             self.step()

@@ -184,6 +184,25 @@ int la_pool_stats(const la_session* s, la_pool_stats_t* out);
  * copied to the host pointer `out`.  Test hook. */
 int la_debug_logits(const la_session* s, float* out, int32_t rows);
 
+/* One step, as la_step, run eagerly with a copy of every intermediate of
+ * the forward pass appended to the device buffer `dev_trace` (test hook:
+ * lets a checker re-run each layer from the engine's own inputs).  Layout,
+ * contiguous, with es = 2 (bf16) or 4 (fp32), M rows, "dt" = model dtype:
+ *   int32 header[16] = {P, M, max_ctx, L, d, H, Hkv, hd, d_ff, vocab, dtype}
+ *   int32 ids[M], int32 pos[M]                    row tokens and positions
+ *   K cache, V cache before the step, each [L][Hkv][max_ctx][hd] dt
+ *   per layer l: x_in f32[M][d], h1 dt[M][d], q dt[M][H*hd] (after RoPE),
+ *                attn_out dt[M][H*hd], x_mid f32[M][d], h2 dt[M][d],
+ *                act dt[M][d_ff]
+ *   x_final f32[M][d], h_final dt[M][d]
+ *   block K, block V, each [L][M][Hkv][hd] dt (after RoPE for K)
+ *   logits f32[M][vocab]
+ * The buffer is caller-owned device memory of at least
+ * la_step_trace_bytes() bytes (LA_ENOMEM otherwise).  Returns as la_step. */
+int la_step_trace(la_session* s, int32_t* out_tokens, int32_t out_cap, int32_t* n_out,
+                  void* dev_trace, size_t bytes);
+int la_step_trace_bytes(const la_session* s, size_t* bytes);
+
 /* Rows in one step (M) of this session. */
 int la_session_rows(const la_session* s, int32_t* rows);
 

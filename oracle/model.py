@@ -55,9 +55,12 @@ class OracleModel:
         self._w = weights
         self._cache: dict[int, np.ndarray] = {}
 
-    # weights are decoded to float64 on demand (the 7B shape does not fit as
-    # float64 all at once on small hosts); `keep` keeps decoded copies.
+    # Weights are decoded to float64 on demand.  keep=True caches the decoded
+    # copies; keep=False (large shapes) decodes each matrix again per use, in
+    # blocks of output features, so float64 copies of a 7B-70B model never
+    # have to exist at once.  Both compute the same products.
     keep = True
+    BLOCK = 2048
 
     def w(self, i: int) -> np.ndarray:
         if i in self._cache:
@@ -67,6 +70,55 @@ class OracleModel:
         if self.keep:
             self._cache[i] = v
         return v
+
+    def _decode_rows(self, i: int, lo: int, hi: int) -> np.ndarray:
+        a = self._w[i][lo:hi]
+        if not self.bf16:
+            return np.asarray(a, dtype=F64)
+        import torch
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+        return t.to(torch.float64).numpy()
+
+    # Accumulation precision of the products: "f64" (default) or "f32".  The
+    # second computes each product in float32 from the same (exactly
+    # representable) operands, the fp32-accumulation reading of the oracle;
+    # the two differ only by rounding, which measures how far apart two
+    # exact evaluations of a bf16 model can drift.
+    acc = "f64"
+
+    def mm(self, x: np.ndarray, i: int) -> np.ndarray:
+        """x @ W_i^T for weight i of shape [out, in]."""
+        if self.acc == "f32":
+            return self._mm32(x, i)
+        if self.keep:
+            return x @ self.w(i).T
+        n_out = self._w[i].shape[0]
+        out = np.empty((x.shape[0], n_out))
+        for lo in range(0, n_out, self.BLOCK):
+            hi = min(n_out, lo + self.BLOCK)
+            out[:, lo:hi] = x @ self._decode_rows(i, lo, hi).T
+        return out
+
+    def _mm32(self, x: np.ndarray, i: int) -> np.ndarray:
+        import torch
+        xf = torch.from_numpy(np.asarray(x, dtype=np.float32))
+        n_out = self._w[i].shape[0]
+        out = np.empty((x.shape[0], n_out))
+        for lo in range(0, n_out, self.BLOCK):
+            hi = min(n_out, lo + self.BLOCK)
+            wf = torch.from_numpy(self._decode_rows(i, lo, hi).astype(np.float32))
+            out[:, lo:hi] = (xf @ wf.T).double().numpy()
+        return out
+
+    def emb_rows(self, tokens: np.ndarray) -> np.ndarray:
+        if self.keep:
+            return self.w(0)[tokens].copy()
+        a = self._w[0][tokens]
+        return decode_bf16(a) if self.bf16 else np.asarray(a, dtype=F64)
+
+    def vec(self, i: int) -> np.ndarray:
+        a = self._w[i]
+        return decode_bf16(a) if self.bf16 else np.asarray(a, dtype=F64)
 
     def rnd(self, x: np.ndarray) -> np.ndarray:
         return bf16_round(x) if self.bf16 else x
@@ -107,6 +159,44 @@ class OracleModel:
             out[:, h, :] = p @ v[:, kh, :]
         return out
 
+    # -- one layer, step by step (forward composes these; a checker can also
+    #    feed each step the inputs another implementation produced) ----------
+    def attn_norm(self, x, li):
+        return self.rnd(self.rmsnorm(x, self.vec(1 + 9 * li)))
+
+    def qkv(self, h, li, positions):
+        """q [T, H, hd], k, v [T, Hkv, hd]; q and k after RoPE."""
+        s, b, T = self.s, 1 + 9 * li, h.shape[0]
+        q = self.mm(h, b + 1).reshape(T, s.n_heads, s.head_dim)
+        k = self.mm(h, b + 2).reshape(T, s.n_kv_heads, s.head_dim)
+        v = self.mm(h, b + 3).reshape(T, s.n_kv_heads, s.head_dim)
+        positions = np.asarray(positions, dtype=np.int64)
+        return self.rnd(self.rope(q, positions)), self.rnd(self.rope(k, positions)), self.rnd(v)
+
+    def attend(self, q, kk, vv, vis):
+        """Attention output [T, H*hd] of rows q over keys/values kk, vv."""
+        T = q.shape[0]
+        return self.rnd(self.attention(q, kk, vv, vis, self.s.n_heads, self.s.n_kv_heads)).reshape(T, -1)
+
+    def attn_residual(self, x, a, li):
+        return x + self.mm(a, 1 + 9 * li + 4)
+
+    def mlp_norm(self, x, li):
+        return self.rnd(self.rmsnorm(x, self.vec(1 + 9 * li + 5)))
+
+    def mlp_act(self, h, li):
+        b = 1 + 9 * li
+        return self.rnd(self.silu(self.mm(h, b + 6)) * self.mm(h, b + 7))
+
+    def mlp_residual(self, x, act, li):
+        return x + self.mm(act, 1 + 9 * li + 8)
+
+    def final_norm(self, x):
+        return self.rnd(self.rmsnorm(x, self.vec(1 + 9 * self.s.n_layers)))
+
+    def lm_head(self, h):
+        return self.mm(h, 2 + 9 * self.s.n_layers)
+
     # -- forward ---------------------------------------------------------
     def forward(self, tokens, positions, vis, past=None):
         """Run rows `tokens` at `positions`.
@@ -117,37 +207,21 @@ class OracleModel:
               S_past + r is row r of this call.
         Returns (logits [T, V] float64, new_kv: list of (K, V) [T, Hkv, hd]).
         """
-        s = self.s
         tokens = np.asarray(tokens, dtype=np.int64)
-        positions = np.asarray(positions, dtype=np.int64)
-        T = tokens.shape[0]
-        H, Hkv, hd = s.n_heads, s.n_kv_heads, s.head_dim
-        x = self.w(0)[tokens].copy()
+        x = self.emb_rows(tokens)
         new_kv = []
-        for li in range(s.n_layers):
-            b = 1 + 9 * li
-            h = self.rnd(self.rmsnorm(x, self.w(b)))
-            q = (h @ self.w(b + 1).T).reshape(T, H, hd)
-            k = (h @ self.w(b + 2).T).reshape(T, Hkv, hd)
-            v = (h @ self.w(b + 3).T).reshape(T, Hkv, hd)
-            q = self.rnd(self.rope(q, positions))
-            k = self.rnd(self.rope(k, positions))
-            v = self.rnd(v)
+        for li in range(self.s.n_layers):
+            h = self.attn_norm(x, li)
+            q, k, v = self.qkv(h, li, positions)
             new_kv.append((k, v))
             if past is not None:
                 kk = np.concatenate([past[li][0], k], axis=0)
                 vv = np.concatenate([past[li][1], v], axis=0)
             else:
                 kk, vv = k, v
-            a = self.rnd(self.attention(q, kk, vv, vis, H, Hkv)).reshape(T, H * hd)
-            x = x + a @ self.w(b + 4).T
-            h = self.rnd(self.rmsnorm(x, self.w(b + 5)))
-            act = self.rnd(self.silu(h @ self.w(b + 6).T) * (h @ self.w(b + 7).T))
-            x = x + act @ self.w(b + 8).T
-        nl = 1 + 9 * s.n_layers
-        h = self.rnd(self.rmsnorm(x, self.w(nl)))
-        logits = h @ self.w(nl + 1).T
-        return logits, new_kv
+            x = self.attn_residual(x, self.attend(q, kk, vv, vis), li)
+            x = self.mlp_residual(x, self.mlp_act(self.mlp_norm(x, li), li), li)
+        return self.lm_head(self.final_norm(x)), new_kv
 
 
 def causal_vis(n_past: int, T: int) -> np.ndarray:

@@ -13,9 +13,11 @@ N(0, 0.02^2) and every norm gain is 1.0.  The initial window is drawn
 uniformly over the vocabulary, following the random initialisation of Jacobi
 iteration (same page, §2 and §3.4 "Mathematical Reformulation").
 
-Weights are drawn with numpy's Philox counter-based generator, keyed by
-(seed, tensor index, chunk index), so any tensor can be regenerated on its own
-and the result does not depend on the number of worker threads.
+Weights are drawn in chunks of 2^22 values; each chunk comes from its own
+torch CPU generator seeded from (seed, tensor index, chunk index), so any
+tensor can be regenerated on its own and the result does not depend on the
+number of worker threads.  bf16 weights are the float32 draws rounded to
+nearest even.
 """
 from __future__ import annotations
 
@@ -101,12 +103,15 @@ def bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
-def _draw_chunk(seed: int, tidx: int, cidx: int, n: int, std: float) -> np.ndarray:
-    key = (int(seed) << 64) | (int(tidx) << 32) | int(cidx)
-    g = np.random.Generator(np.random.Philox(key=key))
-    out = g.standard_normal(n, dtype=np.float32)
-    out *= np.float32(std)
-    return out
+def _draw_chunk(seed: int, tidx: int, cidx: int, n: int, std: float, bf16: bool) -> np.ndarray:
+    import torch
+    key = ((int(seed) * 1000003 + int(tidx)) * 1000033 + int(cidx)) & ((1 << 63) - 1)
+    g = torch.Generator().manual_seed(key)
+    t = torch.randn(n, generator=g, dtype=torch.float32)
+    t.mul_(std)
+    if bf16:
+        return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
 
 
 def gen_tensor(s: ModelShape, seed: int, tidx: int, threads: int | None = None) -> np.ndarray:
@@ -127,17 +132,22 @@ def gen_tensor(s: ModelShape, seed: int, tidx: int, threads: int | None = None) 
     def work(c):
         lo = c * _CHUNK
         hi = min(n, lo + _CHUNK)
-        v = _draw_chunk(seed, tidx, c, hi - lo, s.init_std)
-        out[lo:hi] = bf16_bits(v) if s.dtype == "bf16" else v
+        out[lo:hi] = _draw_chunk(seed, tidx, c, hi - lo, s.init_std, s.dtype == "bf16")
 
     if threads is None:
         threads = min(16, os.cpu_count() or 1)
-    if nch == 1 or threads <= 1:
-        for c in range(nch):
-            work(c)
-    else:
-        with ThreadPoolExecutor(max_workers=threads) as ex:
-            list(ex.map(work, range(nch)))
+    import torch
+    prev = torch.get_num_threads()
+    torch.set_num_threads(1)  # parallelism comes from the chunk pool
+    try:
+        if nch == 1 or threads <= 1:
+            for c in range(nch):
+                work(c)
+        else:
+            with ThreadPoolExecutor(max_workers=threads) as ex:
+                list(ex.map(work, range(nch)))
+    finally:
+        torch.set_num_threads(prev)
     return out.reshape(shape)
 
 

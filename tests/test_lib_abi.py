@@ -95,6 +95,11 @@ def test_step_null_args():
     lib = B.load_library()
     n = ctypes.c_int32()
     assert lib.la_step(None, None, 4, ctypes.byref(n)) == B.LA_EINVAL
+    buf = (ctypes.c_int32 * 4)()
+    assert lib.la_step_trace(None, buf, 4, ctypes.byref(n), None, 0) == B.LA_EINVAL
+    assert lib.la_step_trace(None, buf, 4, ctypes.byref(n), 256, 1 << 20) == B.LA_EINVAL
+    nb = ctypes.c_size_t()
+    assert lib.la_step_trace_bytes(None, ctypes.byref(nb)) == B.LA_EINVAL
 
 
 def test_kernel_hooks_validate():
@@ -110,3 +115,17 @@ def test_kernel_hooks_validate():
     # bf16 GEMM needs K % 64 == 0
     assert lib.la_kernel_gemm(P, 4, 100, P, 64, P, B.LA_BF16, None, 0, None) == B.LA_EINVAL
     assert B.la_kernel_gemm_ws_bytes(121, 4096, 4096) > 0
+
+
+def test_binding_constants_match_header():
+    """Every numeric constant la.h defines has the same value in the binding."""
+    import re
+    text = open(os.path.join(os.path.dirname(__file__), "..", "include", "la.h")).read()
+    consts = {m.group(1): int(m.group(2)) for m in
+              re.finditer(r"^#define (LA_[A-Z_0-9]+) (-?\d+)u?\b", text, re.M)}
+    consts.update({m.group(1): int(m.group(2)) for m in
+                   re.finditer(r"^\s+(LA_[A-Z_0-9]+) = (-?\d+),?", text, re.M)
+                   if not m.group(1).startswith("LA_PROF_")})
+    assert len(consts) >= 12
+    for k, v in consts.items():
+        assert getattr(B, k) == v, k

@@ -193,3 +193,27 @@ def test_bf16_mode_rounds_stored_tensors():
     lg32, kv32 = om32.forward(toks, np.arange(10), causal_vis(0, 10))
     assert not np.array_equal(kv32[0][0], kv[0][0])
     assert np.max(np.abs(lg - lg32)) < 2e-2
+
+
+@pytest.mark.parametrize("name", ["tiny", "small_bf16"])
+def test_f32_accumulation_mode_and_blocked_products(name):
+    """The float32-accumulation mode and the blocked (keep=False) products
+    compute the same function as the default (blocking changes only the
+    float64 summation order): the fp32 model agrees to
+    float32 accuracy, and for a bf16 model every stored tensor still obeys
+    the bf16 contract (the logits move only by rounding-boundary flips)."""
+    s = synth.SHAPES[name]
+    w = synth.gen_weights(s, 0)
+    toks = synth.prompt_motif(s.vocab, 4, 4, seed=3)
+    T = len(toks)
+    ref, _ = OracleModel(s, w).forward(toks, np.arange(T), causal_vis(0, T))
+    m = OracleModel(s, w)
+    m.keep = False
+    m.BLOCK = 96          # several blocks and a ragged last one
+    blk, _ = m.forward(toks, np.arange(T), causal_vis(0, T))
+    np.testing.assert_allclose(blk, ref, rtol=0, atol=1e-12)   # BLAS order only
+    m.acc = "f32"
+    f32, _ = m.forward(toks, np.arange(T), causal_vis(0, T))
+    scale = np.abs(ref).max()
+    tol = 1e-5 if s.dtype == "f32" else 2e-2
+    assert 0 < np.abs(f32 - ref).max() <= tol * max(scale, 1.0)
