@@ -161,7 +161,7 @@ __global__ __launch_bounds__(64) void k_attn_tail(AttnDesc a) {
   const int Pc = a.Pdev ? *a.Pdev : a.P_host;
   const int pos = row_pos(a, r, Pc);
   const int P = a.causal_cache ? pos + 1 : Pc;
-  const int F = a.chunk > 0 ? bulk_end(pos, P, a.D) : 0;
+  const int F = a.mfma ? bulk_end(pos, P, a.D) : 0;
   const int ldb = a.Hkv * HD;
   const T* q = (const T*)a.q + (size_t)r * a.H * HD + h * HD;
   const T* kc = (const T*)a.kc + (size_t)kvh * a.ld_ctx * HD;
@@ -240,7 +240,7 @@ __global__ __launch_bounds__(64) void k_attn_tail(AttnDesc a) {
   float m = -INFINITY, l = 0.f, oo[DPL];
 #pragma unroll
   for (int j = 0; j < DPL; ++j) oo[j] = 0.f;
-  for (int sp = 0; a.chunk > 0 && sp * a.chunk < F; ++sp) {
+  for (int sp = 0; a.mfma && attn_chunk_start(sp) < F; ++sp) {
     const size_t pb = ((size_t)sp * a.rows + r) * a.H + h;
     const float ms = a.part_ml[pb * 2], lsum = a.part_ml[pb * 2 + 1];
     const float mn = fmaxf(m, ms);
@@ -267,7 +267,7 @@ __global__ __launch_bounds__(64) void k_attn_tail(AttnDesc a) {
     for (int j = 0; j < DPL; ++j) st_f(out + d0 + j, oo[j] * inv);
 }
 
-// MFMA part (bf16, head_dim 128): one workgroup per (head, chunk of `chunk`
+// MFMA part (bf16, head_dim 128): one workgroup per (head, prefix chunk
 // committed positions, block of 128 rows).  Each 64-position tile of K and V
 // is staged in LDS once and used by every row; wave w handles the 16-row
 // groups w and w+4.
@@ -295,7 +295,7 @@ __global__ __launch_bounds__(256) void k_attn_bulk(AttnDesc a) {
   const int row0 = rb * 128;
   const int nrows = min(128, a.rows - row0);
   const int ngroups = (nrows + 15) >> 4;
-  const int s0 = split * a.chunk;
+  const int s0 = attn_chunk_start(split);
   const bf16_t* kc = (const bf16_t*)a.kc + (size_t)kvh * a.ld_ctx * 128;
   const bf16_t* vc = (const bf16_t*)a.vc + (size_t)kvh * a.ld_ctx * 128;
   const float scale = 1.0f / sqrtf(128.0f);
@@ -338,7 +338,7 @@ __global__ __launch_bounds__(256) void k_attn_bulk(AttnDesc a) {
   __syncthreads();
   atomicMax(&s_fmax, max(F[0], F[1]));
   __syncthreads();
-  tend = min(s0 + a.chunk, s_fmax);
+  tend = min(attn_chunk_start(split + 1), s_fmax);
 
   for (int t0 = s0; t0 < tend; t0 += AT) {
     // stage K [key][dim] and V^T [dim][key] for positions t0 .. t0+63
@@ -539,10 +539,7 @@ __global__ __launch_bounds__(256) void k_argmax(const float* logits, int V, int3
 
 }  // namespace
 
-int attn_chunk(int ctx, int dtype, int hd) {
-  if (dtype != LA_BF16 || hd != 128) return 0;
-  return ctx <= 1024 ? 128 : ctx <= 4096 ? 256 : 512;
-}
+int attn_uses_mfma(int dtype, int hd) { return dtype == LA_BF16 && hd == 128; }
 
 size_t attn_part_floats(int nsplit, int rows, int H, int hd) {
   return (size_t)nsplit * rows * H * (hd + 2) + (size_t)rows * H * (hd + 2);
@@ -550,8 +547,8 @@ size_t attn_part_floats(int nsplit, int rows, int H, int hd) {
 
 hipError_t launch_attention(const AttnDesc& a, int dtype, hipStream_t st) {
   dim3 grid(a.H, a.rows);
-  if (a.chunk > 0) {
-    if (dtype != LA_BF16 || a.hd != 128 || a.chunk % AT || a.nsplit < 1)
+  if (a.mfma) {
+    if (dtype != LA_BF16 || a.hd != 128 || a.nsplit < 1)
       return hipErrorInvalidValue;
     hipLaunchKernelGGL(k_attn_bulk, dim3(a.H, a.nsplit, (a.rows + 127) / 128), dim3(256), 0, st,
                        a);

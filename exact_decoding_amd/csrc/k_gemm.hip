@@ -49,7 +49,8 @@ __device__ __forceinline__ void lds_barrier() {
 //    registers and issues no other global load until its stores at the end,
 //    so its in-order load counter never makes it wait on anything but the
 //    chunk it is about to use.  The weight stream runs on across the block
-//    boundary; there the accumulators of block bA are parked in registers;
+//    boundary; there the accumulators of block bA are parked in LDS (LDS
+//    traffic does not touch that counter);
 //  * wave 4 (producer) stages the x tile of each chunk into a ring of XR LDS
 //    stages, XR-1 chunks ahead of the consumers, from a 2-deep register ring.
 // One barrier per chunk; the producer writes the stage the consumers left
@@ -69,6 +70,7 @@ template <int MT>
 __global__ __launch_bounds__(320) void k_gemm_bf16(GemmDesc g) {
   constexpr int XSTAGE = MT * 16 * 64;  // bf16 per x stage
   __shared__ __align__(16) bf16_t xs[XR * XSTAGE];
+  __shared__ __align__(16) f32x4_t park[4 * MT * 2 * 64];  // block bA's sums, per consumer
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, q = lane >> 4;
@@ -84,31 +86,42 @@ __global__ __launch_bounds__(320) void k_gemm_bf16(GemmDesc g) {
   const int row0 = mb * 128;
   const int xrows = g.rows - row0;  // valid rows in this row block
 
+  // column placement of consumer wave cw's 32 columns of column block b
+  auto placement = [&](int b, int cw, int& sbase, int& segn, int& nl, int& si)
+      __attribute__((always_inline)) {
+    const int col0 = b * NWG;
+    si = 0;
+    sbase = 0;
+    while (si < g.nseg - 1 && col0 >= sbase + g.seg[si].n) { sbase += g.seg[si].n; ++si; }
+    segn = g.seg[si].n;
+    nl = col0 - sbase + cw * 32;
+  };
   if (wave == 4) {
     // ---------------- producer: x tiles -> LDS ring ----------------
     constexpr int NP = MT * 2;  // 16-byte pieces per lane per chunk
-    const bf16_t* X = (const bf16_t*)g.x;
-    const bf16_t* xp[NP];
-    int lo[NP];
+    // piece j of a lane: row lane/8 + 8j (clamped to the valid rows for the
+    // global read), 16-byte piece lane%8; its swizzled LDS slot depends on
+    // j only through j's parity, so two bases serve all j
+    const bf16_t* X = (const bf16_t*)g.x + (size_t)row0 * K + (lane & 7) * 8;
+    int xo[NP];
 #pragma unroll
     for (int j = 0; j < NP; ++j) {
-      const int pi = lane + 64 * j;
-      const int row = pi >> 3, pc = pi & 7;
-      const int rc = row < xrows ? row : xrows - 1;
-      xp[j] = X + (size_t)(row0 + rc) * K + pc * 8;
-      lo[j] = row * 64 + xswz(row, pc) * 8;
+      const int row = (lane >> 3) + 8 * j;
+      xo[j] = (row < xrows ? row : xrows - 1) * K;
     }
+    const int lo0 = (lane >> 3) * 64 + xswz(lane >> 3, lane & 7) * 8;
+    const int lo1 = ((lane >> 3) + 8) * 64 + xswz((lane >> 3) + 8, lane & 7) * 8 - 512;
     u32x4_t ring[2][NP];
     // chunk t of the run reads K chunk cA + t of block bA, or t - nA of bA + 1
     auto load = [&](int t, u32x4_t (&dst)[NP]) __attribute__((always_inline)) {
       const int kc = t < nA ? cA + t : t - nA;
 #pragma unroll
-      for (int j = 0; j < NP; ++j) dst[j] = *(const u32x4_t*)(xp[j] + (size_t)kc * KC);
+      for (int j = 0; j < NP; ++j) dst[j] = *(const u32x4_t*)(X + xo[j] + kc * KC);
     };
     auto store = [&](int t, const u32x4_t (&src)[NP]) __attribute__((always_inline)) {
       bf16_t* st = xs + (t % XR) * XSTAGE;
 #pragma unroll
-      for (int j = 0; j < NP; ++j) *(u32x4_t*)(st + lo[j]) = src[j];
+      for (int j = 0; j < NP; ++j) *(u32x4_t*)(st + ((j & 1) ? lo1 : lo0) + 512 * j) = src[j];
     };
     // prologue: stages for chunks 0 .. XR-2, ring for the next two
     for (int t = 0; t < n && t < XR - 1; ++t) {
@@ -138,9 +151,7 @@ __global__ __launch_bounds__(320) void k_gemm_bf16(GemmDesc g) {
         if (slot == 0) load(t + XR + 1, ring[0]); else load(t + XR + 1, ring[1]);
       }
     }
-    return;
-  }
-
+  } else {
   // ---------------- consumers: weights + MFMA ----------------
   // this wave's columns of column block b: matrix segment, its first column,
   // and the packed stripe pointers of its two 16-column tiles.  A stripe past
@@ -149,13 +160,9 @@ __global__ __launch_bounds__(320) void k_gemm_bf16(GemmDesc g) {
   // instead of draining them at branch joins.
   auto setup = [&](int b, const bf16_t* (&wrow)[2], int& sbase, int& segn, int& nl)
       __attribute__((always_inline)) {
-    const int col0 = b * NWG;
-    int si = 0;
-    sbase = 0;
-    while (si < g.nseg - 1 && col0 >= sbase + g.seg[si].n) { sbase += g.seg[si].n; ++si; }
+    int si;
+    placement(b, wave, sbase, segn, nl, si);
     const bf16_t* W = (const bf16_t*)g.seg[si].w;
-    segn = g.seg[si].n;
-    nl = col0 - sbase + wave * 32;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int stripe = (nl + t * 16) >> 4;
@@ -174,7 +181,8 @@ __global__ __launch_bounds__(320) void k_gemm_bf16(GemmDesc g) {
     return t < nA ? wA[tt] + (size_t)(cA + t) * 1024 : wB[tt] + (size_t)(t - nA) * 1024;
   };
 
-  f32x4_t acc[MT][2], accA[MT][2];
+  f32x4_t acc[MT][2];
+  f32x4_t* pk = park + (size_t)wave * MT * 2 * 64 + lane;
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
@@ -190,12 +198,11 @@ __global__ __launch_bounds__(320) void k_gemm_bf16(GemmDesc g) {
     }
   };
   // A-fragment offsets (bf16) in a stage: row i*16 + r, k 32j + 8q .. +8
-  // (16-byte piece 4j + q)
-  int aoff[MT][2];
+  // (16-byte piece 4j + q).  The swizzle of row i*16 + r does not depend on
+  // i, so the offset is a per-j base plus i*1024.
+  int abase[2];
 #pragma unroll
-  for (int i = 0; i < MT; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) aoff[i][j] = (i * 16 + r) * 64 + xswz(i * 16 + r, 4 * j + q) * 8;
+  for (int j = 0; j < 2; ++j) abase[j] = r * 64 + xswz(r, 4 * j + q) * 8;
 
   auto chunk = [&](int t, u32x4_t (&w)[2][2], bool more_w) __attribute__((always_inline)) {
     if (t == nA) {
@@ -204,7 +211,7 @@ __global__ __launch_bounds__(320) void k_gemm_bf16(GemmDesc g) {
       for (int i = 0; i < MT; ++i)
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-          accA[i][tt] = acc[i][tt];
+          pk[(i * 2 + tt) * 64] = acc[i][tt];
           acc[i][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
     }
@@ -218,7 +225,7 @@ __global__ __launch_bounds__(320) void k_gemm_bf16(GemmDesc g) {
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
         U4B a;
-        a.u = *(const u32x4_t*)(st + aoff[i][j]);
+        a.u = *(const u32x4_t*)(st + abase[j] + i * 1024);
         acc[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b0.v, acc[i][0], 0, 0, 0);
         acc[i][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b1.v, acc[i][1], 0, 0, 0);
       }
@@ -266,11 +273,16 @@ __global__ __launch_bounds__(320) void k_gemm_bf16(GemmDesc g) {
   };
   const int slotA = wg - plan_first_wg(g.sp, bA);
   if (n > nA) {
-    store_block(accA, slotA, sbA, segnA, nlA);
     store_block(acc, 0, sbB, segnB, nlB);
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) acc[i][tt] = pk[(i * 2 + tt) * 64];
+    store_block(acc, slotA, sbA, segnA, nlA);
   } else {
     store_block(acc, slotA, sbA, segnA, nlA);
   }
+  }  // consumers
 }
 
 // fp32 models: one thread per output element, K summed in order.
@@ -355,10 +367,7 @@ __global__ __launch_bounds__(256) void k_qkv_epi(QkvEpi e) {
   }
 }
 
-// x[m] += sum of the split partials; then h[m] = x[m] / sqrt(mean(x^2) + eps) * g
-// (the residual add fused with the next RMSNorm).  Thread t owns columns
-// t, t+256, ...; the sum of squares is reduced in a fixed tree.
-// x[m] += sum of the split partials (in split order); then
+// x[m] += sum of the pieces (in K order); then
 // h[m] = x[m] / sqrt(mean(x^2) + eps) * g: the residual add fused with the
 // next RMSNorm.  One workgroup of d/NC threads per row; thread t owns columns
 // t + j*blockDim; the sum of squares is reduced in a fixed order (within a
@@ -454,7 +463,9 @@ SplitPlan gemm_plan(int N, int K, int dtype) {
   // rounds of LA_GEMM_TARGET_WG workgroups (one per CU); otherwise deal the
   // units out to full rounds, keeping >= 4 chunks per workgroup, <= 15
   // pieces per block on average, and >= nblk workgroups (so a run spans at
-  // most two column blocks).
+  // most two column blocks).  (Measured: a uniform K split with fewer
+  // pieces, e.g. 2 x 96 workgroups for the 7B QKV product, is slower
+  // overall, epilogue included, than the even deal over 256.)
   const int T = LA_GEMM_TARGET_WG;
   const int rounds = (p.nblk + T - 1) / T;
   const long long U = (long long)p.nblk * p.nch;

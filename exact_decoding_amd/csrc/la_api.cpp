@@ -84,7 +84,7 @@ struct Shape {
   int N, W, G, cap;
   SplitPlan sp_qkv, sp_o, sp_gu, sp_d, sp_lm;
   double pc_qkv, pc_o, pc_gu, pc_d;  // mean pieces per column block (profile bytes)
-  int att_chunk, att_nsplit;  // MFMA-attention chunking (0 = per-row kernel only)
+  int att_mfma, att_nsplit;  // MFMA-attention prefix chunks (0 = per-row kernel only)
 };
 
 Shape make_shape(const la_model* m, const la_decode_params* p) {
@@ -116,8 +116,8 @@ Shape make_shape(const la_model* m, const la_decode_params* p) {
   s.pc_o = mean_pieces(s.sp_o);
   s.pc_gu = mean_pieces(s.sp_gu);
   s.pc_d = mean_pieces(s.sp_d);
-  s.att_chunk = attn_chunk(s.ld_ctx, s.dt, s.hd);
-  s.att_nsplit = s.att_chunk ? (s.ld_ctx + s.att_chunk - 1) / s.att_chunk : 0;
+  s.att_mfma = attn_uses_mfma(s.dt, s.hd);
+  s.att_nsplit = s.att_mfma ? attn_nchunks(s.ld_ctx) : 0;
   return s;
 }
 
@@ -140,7 +140,7 @@ Views plan_views(const Shape& s) {
   v.h = w.take(R * s.d * es);
   v.q = w.take(R * s.H * s.hd * es);
   v.att = w.take(R * s.H * s.hd * es);
-  v.att_part = w.take((s.att_chunk ? attn_part_floats(s.att_nsplit, (int)R, s.H, s.hd) : 1) * 4);
+  v.att_part = w.take((s.att_mfma ? attn_part_floats(s.att_nsplit, (int)R, s.H, s.hd) : 1) * 4);
   v.act = w.take(R * s.F * es);
   v.part = w.take(part);
   v.logits = w.take((size_t)s.M * s.V * 4);
@@ -347,9 +347,9 @@ int enqueue_forward(la_session* ss, int rows, bool mode_prefill) {
     a.causal_cache = mode_prefill ? 1 : 0;
     a.lay = ss->lay;
     a.D = s.N - 1;
-    a.chunk = s.att_chunk;
+    a.mfma = s.att_mfma;
     a.nsplit = s.att_nsplit;
-    if (a.chunk) {
+    if (a.mfma) {
       a.part_o = ss->at<float>(ss->v.att_part);
       a.part_ml = a.part_o + (size_t)a.nsplit * rows * s.H * s.hd;
       a.tail_o = a.part_ml + (size_t)a.nsplit * rows * s.H * 2;
@@ -767,10 +767,9 @@ int la_debug_logits(const la_session* s, float* out, int32_t rows) {
 size_t la_kernel_attention_ws_bytes(int32_t ld_ctx, int32_t H, int32_t hd, int32_t N, int32_t W,
                                     int32_t G, int32_t dtype) {
   if (ld_ctx < 0 || H < 1 || N < 2 || W < 0 || G < 0) return 0;
-  const int chunk = attn_chunk(ld_ctx, dtype, hd);
-  if (!chunk) return 0;
+  if (!attn_uses_mfma(dtype, hd)) return 0;
   const int M = 1 + (W + G) * (N - 1);
-  const int nsplit = (ld_ctx + chunk - 1) / chunk;
+  const int nsplit = attn_nchunks(ld_ctx);
   return attn_part_floats(nsplit > 0 ? nsplit : 1, M, H, hd) * 4;
 }
 
@@ -795,9 +794,9 @@ int la_kernel_attention(const void* q, const void* k_cache, const void* v_cache,
   a.causal_cache = 0;
   a.lay = RowLayout{N, W, G, (int)M};
   a.D = N - 1;
-  a.chunk = attn_chunk(ld_ctx, dtype, hd);
-  if (a.chunk) {
-    a.nsplit = (ld_ctx + a.chunk - 1) / a.chunk;
+  a.mfma = attn_uses_mfma(dtype, hd);
+  if (a.mfma) {
+    a.nsplit = attn_nchunks(ld_ctx);
     if (a.nsplit < 1) a.nsplit = 1;
     const size_t need = attn_part_floats(a.nsplit, (int)M, H, hd) * 4;
     if (!ws || ws_bytes < need) return fail(LA_ENOMEM, "attention workspace too small");

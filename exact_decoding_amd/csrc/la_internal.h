@@ -150,11 +150,11 @@ struct AttnDesc {
   int causal_cache;    // 1: every key 0..pos(row) is in the cache (prefill)
   RowLayout lay;
   // Split of each row's keys: the committed tiles [0, F) go through the MFMA
-  // kernel in chunks of `chunk` positions, [F, pos] through the per-row
+  // kernel in the chunks of attn_chunk_start, [F, pos] through the per-row
   // kernel; F = min(floor((pos - D) / 64) * 64, floor(P / 64) * 64).
-  // chunk == 0: no MFMA part (F = 0).
+  // mfma == 0: no MFMA part (F = 0).
   int D;
-  int chunk;
+  int mfma;
   int nsplit;          // chunks allocated in part_* (grid of the MFMA kernel)
   float* part_o;       // [nsplit][rows][H][hd] unnormalised outputs
   float* part_ml;      // [nsplit][rows][H][2] running max, sum
@@ -162,7 +162,21 @@ struct AttnDesc {
   float* tail_ml;      // [rows][H][2]
 };
 hipError_t launch_attention(const AttnDesc& a, int dtype, hipStream_t st);
-int attn_chunk(int ctx, int dtype, int hd);
+// Whether the MFMA kernel takes the shared prefix (bf16, head_dim 128).
+int attn_uses_mfma(int dtype, int hd);
+// The shared prefix of a row is split into chunks on a fixed partition of
+// absolute positions (128 wide below 1024, 256 wide below 4096, 512 wide
+// after), so a row's arithmetic depends on its position only, never on the
+// session's context capacity.
+__host__ __device__ inline int attn_chunk_start(int s) {
+  return s <= 8 ? 128 * s : s <= 20 ? 1024 + 256 * (s - 8) : 4096 + 512 * (s - 20);
+}
+__host__ __device__ inline int attn_nchunks(int L) {  // chunks meeting [0, L)
+  if (L <= 0) return 0;
+  if (L <= 1024) return (L + 127) / 128;
+  if (L <= 4096) return 8 + (L - 1024 + 255) / 256;
+  return 20 + (L - 4096 + 511) / 512;
+}
 size_t attn_part_floats(int nsplit, int rows, int H, int hd);
 
 // lookahead bookkeeping kernels

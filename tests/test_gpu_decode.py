@@ -121,3 +121,24 @@ def test_bf16_lookahead_bit_exact_and_oracle(name, N, W, G):
     sure = margin > 2 * tol
     assert np.array_equal(np.array(ar_toks)[sure], top[sure])
     gm.close()
+
+
+def test_bf16_exact_whatever_the_context_capacity():
+    """A row's attention arithmetic depends on its position only: a lookahead
+    session and an AR session with very different max_ctx (so different
+    sizes of every context-sized buffer) emit identical tokens, with
+    positions crossing the 1024 boundary of the prefix chunk partition."""
+    s = synth.SHAPES["small_bf16"]
+    gm = Model(s, synth.gen_weights(s, 0))
+    prompt = synth.prompt_zipf_spans(s.vocab, length=1000, seed=5)
+    n_new = 48
+    la_ses = gm.session(prompt, 5, 7, 7, n_new, window=synth.gen_window(5, 7, s.vocab, seed=2),
+                        prompt_ref=True, max_ctx=len(prompt) + n_new + 20)
+    la_toks = la_ses.decode()
+    la_ses.close()
+    ar_ses = gm.session(prompt, 5, 7, 7, n_new, ar=True, max_ctx=6000)
+    ar_toks = ar_ses.decode()
+    ar_ses.close()
+    gm.close()
+    assert len(la_toks) == n_new
+    assert la_toks == ar_toks
