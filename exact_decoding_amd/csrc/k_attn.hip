@@ -340,27 +340,34 @@ __global__ __launch_bounds__(256) void k_attn_bulk(AttnDesc a) {
   __syncthreads();
   tend = min(attn_chunk_start(split + 1), s_fmax);
 
+  // K [key][dim] and V^T [dim][key] of a 64-position tile: each thread holds
+  // 32 dims of one key of K and 16 dims of a key pair of V, fetched one tile
+  // ahead so the loads of tile t+1 overlap the arithmetic of tile t
+  const int fkey = tid >> 2, fseg = tid & 3;  // K: 32 dims per thread
+  const int fkp = tid & 31, fvs = tid >> 5;   // V: key pair, 16-dim segment
+  u32x4_t kf[4];
+  U4 va0, va1, vb0, vb1;
+  auto fetch = [&](int t0) __attribute__((always_inline)) {
+    const u32x4_t* src = (const u32x4_t*)(kc + (size_t)(t0 + fkey) * 128 + fseg * 32);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) kf[j] = src[j];
+    const u32x4_t* v0 = (const u32x4_t*)(vc + (size_t)(t0 + 2 * fkp) * 128 + fvs * 16);
+    const u32x4_t* v1 = (const u32x4_t*)(vc + (size_t)(t0 + 2 * fkp + 1) * 128 + fvs * 16);
+    va0.u = v0[0]; va1.u = v0[1]; vb0.u = v1[0]; vb1.u = v1[1];
+  };
+  if (s0 < tend) fetch(s0);
   for (int t0 = s0; t0 < tend; t0 += AT) {
-    // stage K [key][dim] and V^T [dim][key] for positions t0 .. t0+63
-    {
-      const int key = tid >> 2, seg = tid & 3;  // 32 dims per thread
-      const u32x4_t* src = (const u32x4_t*)(kc + (size_t)(t0 + key) * 128 + seg * 32);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) *(u32x4_t*)(&Ks[key * KSTR + seg * 32 + j * 8]) = src[j];
-      const int kp = tid & 31, vs = tid >> 5;  // key pair, 16-dim segment
-      const u32x4_t* v0 = (const u32x4_t*)(vc + (size_t)(t0 + 2 * kp) * 128 + vs * 16);
-      const u32x4_t* v1 = (const u32x4_t*)(vc + (size_t)(t0 + 2 * kp + 1) * 128 + vs * 16);
-      U4 a0, a1, b0, b1;
-      a0.u = v0[0]; a1.u = v0[1]; b0.u = v1[0]; b1.u = v1[1];
+    for (int j = 0; j < 4; ++j) *(u32x4_t*)(&Ks[fkey * KSTR + fseg * 32 + j * 8]) = kf[j];
 #pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        *(uint32_t*)(&Vt[(vs * 16 + d) * VSTR + 2 * kp]) =
-            (uint32_t)a0.h[d] | ((uint32_t)b0.h[d] << 16);
-        *(uint32_t*)(&Vt[(vs * 16 + 8 + d) * VSTR + 2 * kp]) =
-            (uint32_t)a1.h[d] | ((uint32_t)b1.h[d] << 16);
-      }
+    for (int d = 0; d < 8; ++d) {
+      *(uint32_t*)(&Vt[(fvs * 16 + d) * VSTR + 2 * fkp]) =
+          (uint32_t)va0.h[d] | ((uint32_t)vb0.h[d] << 16);
+      *(uint32_t*)(&Vt[(fvs * 16 + 8 + d) * VSTR + 2 * fkp]) =
+          (uint32_t)va1.h[d] | ((uint32_t)vb1.h[d] << 16);
     }
     __syncthreads();
+    if (t0 + AT < tend) fetch(t0 + AT);
 #pragma unroll
     for (int gi = 0; gi < 2; ++gi) {
       if (!gon[gi]) continue;
