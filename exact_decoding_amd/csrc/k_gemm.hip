@@ -285,6 +285,248 @@ __global__ __launch_bounds__(320) void k_gemm_bf16(GemmDesc g) {
   }  // consumers
 }
 
+// Four symmetric waves, one per SIMD (so each may hold up to 512 registers).
+// Same work split, packed weights and column ownership as k_gemm_bf16 (each
+// wave: 32 columns, all MT row tiles), but no producer wave:
+//  * every thread stages 1/256 of the x tile of each chunk; its x pieces ride
+//    in the same in-order load pipeline as its weights, PF chunks ahead
+//    (chunk t+1+PF's x right after chunk t+PF's weights), so a wave only
+//    ever waits for the oldest loads it issued;
+//  * two LDS stages: x(t+1) is written before the barrier of iteration t and
+//    its A fragments are read right after it, while the MFMAs of chunk t run
+//    on the fragments read one iteration earlier.  A stage is rewritten two
+//    iterations after its last read, and every barrier waits on the wave's
+//    LDS traffic, so no extra synchronisation is needed.
+template <int MT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_gemm4(GemmDesc g) {
+  constexpr int XSTAGE = MT * 16 * 64;  // bf16 per x stage
+  constexpr int NPC = MT * 128;         // 16-byte x pieces per chunk
+  constexpr int XJ = (NPC + 255) / 256; // pieces per thread per chunk
+  static_assert(PF % 2 == 0, "the A-fragment buffers alternate with the chunk parity");
+  __shared__ __align__(16) bf16_t xs[2 * XSTAGE];
+  // per wave: its 32 columns x 16*MT rows of sums, rows padded to PKS floats
+  // (16-byte aligned; the 4 row groups of an MFMA tile land on distinct
+  // banks).  Sums leave through it as 128-byte row segments.
+  constexpr int PKS = 36;
+  __shared__ __align__(16) float park[4 * MT * 16 * PKS];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, q = lane >> 4;
+  const int wg = blockIdx.x, mb = blockIdx.z;
+  const int K = g.K;
+  const int nch = g.sp.nch;
+  const int U = g.sp.nblk * nch;
+  const int u0 = (int)((long long)wg * U / g.sp.G);
+  const int u1 = (int)((long long)(wg + 1) * U / g.sp.G);
+  const int n = u1 - u0;
+  const int bA = u0 / nch, cA = u0 - bA * nch;
+  const int nA = min(n, nch - cA);
+  const int row0 = mb * 128;
+  const int xrows = g.rows - row0;
+
+  // ---- x pieces of this thread: piece tid + 256j of the chunk (row p/8,
+  // 16-byte piece p%8, swizzled in LDS); a piece past the tile (odd MT)
+  // reloads the last one and is not written
+  const bf16_t* X = (const bf16_t*)g.x + (size_t)row0 * K;
+  int xo[XJ], xl[XJ];
+  bool xw[XJ];
+#pragma unroll
+  for (int j = 0; j < XJ; ++j) {
+    const int pid = tid + 256 * j;
+    xw[j] = pid < NPC;
+    const int pc = xw[j] ? pid : NPC - 1;
+    const int row = pc >> 3, piece = pc & 7;
+    xo[j] = (row < xrows ? row : xrows - 1) * K + piece * 8;
+    xl[j] = row * 64 + xswz(row, piece) * 8;
+  }
+  auto load_x = [&](int t, u32x4_t (&dst)[XJ]) __attribute__((always_inline)) {
+    const int tc = t < n ? t : n - 1;
+    const int kc = tc < nA ? cA + tc : tc - nA;
+#pragma unroll
+    for (int j = 0; j < XJ; ++j) dst[j] = *(const u32x4_t*)(X + xo[j] + kc * KC);
+  };
+  auto store_x = [&](int t, const u32x4_t (&src)[XJ]) __attribute__((always_inline)) {
+    bf16_t* st = xs + (t & 1) * XSTAGE;
+#pragma unroll
+    for (int j = 0; j < XJ; ++j)
+      if (xw[j]) *(u32x4_t*)(st + xl[j]) = src[j];
+  };
+
+  // ---- weights: this wave's two 16-column stripes of column block b
+  auto placement = [&](int b, int& sbase, int& segn, int& nl, int& si)
+      __attribute__((always_inline)) {
+    const int col0 = b * NWG;
+    si = 0;
+    sbase = 0;
+    while (si < g.nseg - 1 && col0 >= sbase + g.seg[si].n) { sbase += g.seg[si].n; ++si; }
+    segn = g.seg[si].n;
+    nl = col0 - sbase + wave * 32;
+  };
+  auto setup = [&](int b, const bf16_t* (&wrow)[2], int& sbase, int& segn, int& nl)
+      __attribute__((always_inline)) {
+    int si;
+    placement(b, sbase, segn, nl, si);
+    const bf16_t* W = (const bf16_t*)g.seg[si].w;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int stripe = (nl + t * 16) >> 4;
+      const int ok = nl + t * 16 < segn;
+      wrow[t] = W + (size_t)(ok ? stripe : 0) * nch * 1024 + lane * 8;
+    }
+  };
+  const bf16_t* wA[2];
+  const bf16_t* wB[2];
+  int sbA, segnA, nlA, sbB = 0, segnB = 0, nlB = 0;
+  setup(bA, wA, sbA, segnA, nlA);
+  if (n > nA) setup(bA + 1, wB, sbB, segnB, nlB);
+  else { wB[0] = wA[0]; wB[1] = wA[1]; }
+  auto load_w = [&](int t, u32x4_t (&dst)[2][2]) __attribute__((always_inline)) {
+    const int tc = t < n ? t : n - 1;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const bf16_t* p = tc < nA ? wA[tt] + (size_t)(cA + tc) * 1024 : wB[tt] + (size_t)(tc - nA) * 1024;
+      dst[tt][0] = *(const u32x4_t*)p;
+      dst[tt][1] = *(const u32x4_t*)(p + 512);
+    }
+  };
+
+  // ---- A fragments (row i*16 + r, k 32j + 8q .. +8) and the MFMAs
+  int abase[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) abase[j] = r * 64 + xswz(r, 4 * j + q) * 8;
+  auto read_a = [&](int t, U4B (&dst)[MT][2]) __attribute__((always_inline)) {
+    const bf16_t* st = xs + (t & 1) * XSTAGE;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < MT; ++i) dst[i][j].u = *(const u32x4_t*)(st + abase[j] + i * 1024);
+  };
+  f32x4_t acc[MT][2];
+  float* pk = park + wave * MT * 16 * PKS;
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) acc[i][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // MFMA D layout: lane holds rows 4q..4q+3 of column r of each 16x16 tile
+  auto park_acc = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pk[(i * 16 + 4 * q + e) * PKS + tt * 16 + r] = acc[i][tt][e];
+  };
+  auto mfma = [&](const U4B (&a)[MT][2], const u32x4_t (&w)[2][2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      U4B b0, b1;
+      b0.u = w[0][j];
+      b1.u = w[1][j];
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        acc[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i][j].v, b0.v, acc[i][0], 0, 0, 0);
+        acc[i][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i][j].v, b1.v, acc[i][1], 0, 0, 0);
+      }
+    }
+  };
+
+  u32x4_t wr[PF][2][2];
+  u32x4_t xr[PF][XJ];  // x(c) for c >= 1 lives in xr[c % PF]
+  U4B A0[MT][2], A1[MT][2];
+  // one chunk: x(t+1) -> LDS, barrier, A(t+1) <- LDS, MFMAs of chunk t,
+  // then the loads of chunk t+PF (weights) and t+1+PF (x) into the freed slots
+  auto iter = [&](int t, u32x4_t (&w)[2][2], u32x4_t (&xn)[XJ], U4B (&ac)[MT][2],
+                  U4B (&an)[MT][2], bool more) __attribute__((always_inline)) {
+    if (t == nA) {  // first chunk of block bA + 1: park block bA's sums
+      park_acc();
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) acc[i][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    if (t + 1 < n) store_x(t + 1, xn);
+    lds_barrier();
+    if (t + 1 < n) read_a(t + 1, an);
+    mfma(ac, w);
+    if (more) {
+      load_w(t + PF, w);
+      load_x(t + 1 + PF, xn);
+    }
+  };
+
+  {  // prologue: x(0) staged and its fragments read; chunks 0..PF-1 (weights)
+     // and 1..PF (x) in flight, in chunk order
+    u32x4_t x0[XJ];
+    load_x(0, x0);
+#pragma unroll
+    for (int s = 0; s < PF; ++s) {
+      load_w(s, wr[s]);
+      load_x(s + 1, xr[(s + 1) % PF]);
+    }
+    store_x(0, x0);
+    lds_barrier();
+    read_a(0, A0);
+  }
+  int tb = 0;
+  for (; tb + 2 * PF <= n; tb += PF) {
+#pragma unroll
+    for (int s = 0; s < PF; s += 2) {
+      iter(tb + s, wr[s], xr[(s + 1) % PF], A0, A1, true);
+      iter(tb + s + 1, wr[s + 1], xr[(s + 2) % PF], A1, A0, true);
+    }
+  }
+  for (; tb < n; tb += PF) {
+#pragma unroll
+    for (int s = 0; s < PF; s += 2) {
+      if (tb + s < n) iter(tb + s, wr[s], xr[(s + 1) % PF], A0, A1, tb + s + PF < n);
+      if (tb + s + 1 < n) iter(tb + s + 1, wr[s + 1], xr[(s + 2) % PF], A1, A0, tb + s + 1 + PF < n);
+    }
+  }
+
+  // this wave's parked rows -> piece `slot`: lane l writes columns 4(l%8)..+4
+  // of rows l/8, l/8 + 8, ...
+  const bool vec_ok = (g.N & 3) == 0;
+  auto store_rows = [&](int slot, int sbase, int segn, int nl) __attribute__((always_inline)) {
+    float* out = g.part + (size_t)slot * g.rows_pad * g.N;
+    const int c4 = (lane & 7) * 4;
+    const int nloc = nl + c4;
+    if (nloc >= segn) return;
+    const int nr = min(MT * 16, g.rows - row0);
+    for (int rr = lane >> 3; rr < nr; rr += 8) {
+      const f32x4_t v = *(const f32x4_t*)(pk + rr * PKS + c4);
+      float* dst = out + (size_t)(row0 + rr) * g.N + sbase + nloc;
+      if (vec_ok && nloc + 3 < segn) {
+        *(f32x4_t*)dst = v;
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (nloc + k < segn) dst[k] = v[k];
+      }
+    }
+  };
+  auto wave_lds_sync = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  // block bA's piece goes to its slot among the block's pieces; block bA + 1
+  // starts with this run, so its piece is slot 0
+  const int slotA = wg - plan_first_wg(g.sp, bA);
+  if (n > nA) {
+    wave_lds_sync();
+    store_rows(slotA, sbA, segnA, nlA);
+    wave_lds_sync();
+    park_acc();
+    wave_lds_sync();
+    store_rows(0, sbB, segnB, nlB);
+  } else {
+    park_acc();
+    wave_lds_sync();
+    store_rows(slotA, sbA, segnA, nlA);
+  }
+}
+
 // fp32 models: one thread per output element, K summed in order.
 __global__ __launch_bounds__(64) void k_gemm_f32(GemmDesc g) {
   const int n = blockIdx.x * 64 + threadIdx.x;
@@ -497,16 +739,20 @@ hipError_t launch_gemm(const GemmDesc& g, int dtype, hipStream_t st) {
   // the arithmetic of any row
   const int mt = mblk > 1 ? 8 : (rows_last + 15) / 16;
   dim3 grid(g.sp.G, 1, mblk);
-  const dim3 blk(320);
+  // one row tile (the autoregressive step): the producer-wave kernel, which
+  // streams fastest when the MFMA work is small; more rows: the four-wave
+  // kernel.  Both accumulate every output element over the same chunks in
+  // the same MFMA order, so a row's sums do not depend on which one ran.
+  const dim3 b4(256);
   switch (mt) {
-    case 1: hipLaunchKernelGGL(k_gemm_bf16<1>, grid, blk, 0, st, g); break;
-    case 2: hipLaunchKernelGGL(k_gemm_bf16<2>, grid, blk, 0, st, g); break;
-    case 3: hipLaunchKernelGGL(k_gemm_bf16<3>, grid, blk, 0, st, g); break;
-    case 4: hipLaunchKernelGGL(k_gemm_bf16<4>, grid, blk, 0, st, g); break;
-    case 5: hipLaunchKernelGGL(k_gemm_bf16<5>, grid, blk, 0, st, g); break;
-    case 6: hipLaunchKernelGGL(k_gemm_bf16<6>, grid, blk, 0, st, g); break;
-    case 7: hipLaunchKernelGGL(k_gemm_bf16<7>, grid, blk, 0, st, g); break;
-    default: hipLaunchKernelGGL(k_gemm_bf16<8>, grid, blk, 0, st, g); break;
+    case 1: hipLaunchKernelGGL(k_gemm_bf16<1>, grid, dim3(320), 0, st, g); break;
+    case 2: hipLaunchKernelGGL(k_gemm4<2>, grid, b4, 0, st, g); break;
+    case 3: hipLaunchKernelGGL(k_gemm4<3>, grid, b4, 0, st, g); break;
+    case 4: hipLaunchKernelGGL(k_gemm4<4>, grid, b4, 0, st, g); break;
+    case 5: hipLaunchKernelGGL(k_gemm4<5>, grid, b4, 0, st, g); break;
+    case 6: hipLaunchKernelGGL(k_gemm4<6>, grid, b4, 0, st, g); break;
+    case 7: hipLaunchKernelGGL(k_gemm4<7>, grid, b4, 0, st, g); break;
+    default: hipLaunchKernelGGL(k_gemm4<8>, grid, b4, 0, st, g); break;
   }
   return hipGetLastError();
 }
