@@ -76,7 +76,7 @@ def calibrate():
     return gbps
 
 
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "k_gemm_bf16_llama7b_lookahead_pmc.md")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_llama7b_lookahead_pmc.md")
 GEMM_SOURCE = os.path.join(ROOT, "exact_decoding_amd", "csrc", "k_gemm.hip")
 
 
@@ -251,8 +251,8 @@ def main():
                     agg[k][f] += v[f]
     ses.close()
     P_avg = P_sum / max(n_prof, 1)
-    # the dominant kernel is the projection GEMM k_gemm_bf16; its launches are
-    # the four projections per layer plus the LM head
+    # the dominant kernel is the projection GEMM (k_gemm4 at M = 121); its
+    # launches are the four projections per layer plus the LM head
     g = {f: agg["gemm"][f] + agg["lm_head"][f] for f in agg["gemm"]}
     gemm_ms = g["ms"] / g["launches"]
     gemm_bytes = g["bytes"] / g["launches"]
@@ -295,7 +295,8 @@ def main():
         "lookahead_equals_ar": exact,
         "step_hbm": {"bytes_per_step": step_bytes, "GBps": step_gbps, "frac": step_gbps / HBM_PEAK_GBPS,
                      "P_avg": P_avg},
-        "roofline": {"kernel": "k_gemm_bf16 (QKV, O, gate/up, down projections and LM head)", "bound": "hbm",
+        "roofline": {"kernel": "projection GEMM k_gemm4 at M = 121 (QKV, O, gate/up, down and LM head)",
+                     "bound": "hbm",
                      "achieved": gemm_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": gemm_gbps / HBM_PEAK_GBPS, "traffic": gemm_traffic(),
                      "avg_launch_ms": gemm_ms, "avg_launch_bytes": gemm_bytes,

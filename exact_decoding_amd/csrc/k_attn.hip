@@ -177,6 +177,21 @@ __global__ __launch_bounds__(64) void k_attn_tail(AttnDesc a) {
 #pragma unroll
   for (int j = 0; j < DPL; ++j) o[j] = 0.f;
 
+  // the MFMA kernel's partials of the first NPRE chunks of [0, F), loaded
+  // now so their latency overlaps the tile loads below
+  constexpr int NPRE = 4;
+  float pm[NPRE], pl[NPRE], po[NPRE][DPL];
+#pragma unroll
+  for (int sp = 0; sp < NPRE; ++sp) {
+    if (a.mfma && attn_chunk_start(sp) < F) {
+      const size_t pb = ((size_t)sp * a.rows + r) * a.H + h;
+      pm[sp] = a.part_ml[pb * 2];
+      pl[sp] = a.part_ml[pb * 2 + 1];
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) po[sp][j] = down ? a.part_o[pb * HD + d0 + j] : 0.f;
+    }
+  }
+
   // tiles of 64 absolute positions over [F, pos]; lane j holds key 64t + j
   for (int t = F / AT; t <= pos / AT; ++t) {
     const int p = t * AT + lane;
@@ -240,17 +255,25 @@ __global__ __launch_bounds__(64) void k_attn_tail(AttnDesc a) {
   float m = -INFINITY, l = 0.f, oo[DPL];
 #pragma unroll
   for (int j = 0; j < DPL; ++j) oo[j] = 0.f;
-  for (int sp = 0; a.mfma && attn_chunk_start(sp) < F; ++sp) {
-    const size_t pb = ((size_t)sp * a.rows + r) * a.H + h;
-    const float ms = a.part_ml[pb * 2], lsum = a.part_ml[pb * 2 + 1];
+  auto merge = [&](float ms, float lsum, const float (&os)[DPL]) __attribute__((always_inline)) {
     const float mn = fmaxf(m, ms);
     const float ca = m == -INFINITY ? 0.f : expf(m - mn);
     const float cb = expf(ms - mn);
     l = l * ca + lsum * cb;
     if (down)
 #pragma unroll
-      for (int j = 0; j < DPL; ++j) oo[j] = oo[j] * ca + a.part_o[pb * HD + d0 + j] * cb;
+      for (int j = 0; j < DPL; ++j) oo[j] = oo[j] * ca + os[j] * cb;
     m = mn;
+  };
+#pragma unroll
+  for (int sp = 0; sp < NPRE; ++sp)
+    if (a.mfma && attn_chunk_start(sp) < F) merge(pm[sp], pl[sp], po[sp]);
+  for (int sp = NPRE; a.mfma && attn_chunk_start(sp) < F; ++sp) {
+    const size_t pb = ((size_t)sp * a.rows + r) * a.H + h;
+    float os[DPL];
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) os[j] = down ? a.part_o[pb * HD + d0 + j] : 0.f;
+    merge(a.part_ml[pb * 2], a.part_ml[pb * 2 + 1], os);
   }
   {
     const float mn = fmaxf(m, m_run);

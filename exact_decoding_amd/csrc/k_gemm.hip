@@ -17,7 +17,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 namespace {
 
-constexpr int NWG = 128;      // output columns per workgroup (4 waves x 2 tiles x 16)
+constexpr int NWG = GEMM_NWG;  // output columns per workgroup (4 waves x 2 tiles x 16)
 constexpr int KC = 64;        // K per chunk: two 16x16x32 MFMA steps
 #ifndef LA_GEMM_PF
 #define LA_GEMM_PF 4
@@ -541,131 +541,6 @@ __global__ __launch_bounds__(64) void k_gemm_f32(GemmDesc g) {
   g.part[(size_t)m * g.N + n] = acc;
 }
 
-// Sum of the pieces of one output element, in K order.  NP is a
-// compile-time bound (>= the plan's np) so the loads are issued together.
-template <int NP>
-__device__ __forceinline__ float sum_pieces(const float* __restrict__ part, const SplitPlan& sp,
-                                            int rows_pad, int N, int m, int col) {
-  if (NP == 1) return part[(size_t)m * N + col];
-  const int np = plan_pieces(sp, col / NWG);
-  float p[NP];
-#pragma unroll
-  for (int s = 0; s < NP; ++s) p[s] = s < np ? part[((size_t)s * rows_pad + m) * N + col] : 0.f;
-  float v = p[0];
-#pragma unroll
-  for (int s = 1; s < NP; ++s)
-    if (s < np) v += p[s];
-  return v;
-}
-
-#define LA_SPLIT_DISPATCH(NP_, CALL)          \
-  if ((NP_) <= 1) { CALL(1); }                \
-  else if ((NP_) <= 2) { CALL(2); }           \
-  else if ((NP_) <= 4) { CALL(4); }           \
-  else if ((NP_) <= 8) { CALL(8); }           \
-  else if ((NP_) <= 16) { CALL(16); }         \
-  else return hipErrorInvalidValue;
-
-// Sum the K splits of the fused QKV product, rotate q and k (RoPE at the
-// row's position, pairs (i, i + hd/2)) and store q, k, v.  One thread per
-// rotated pair of q/k or per element of v.
-template <typename T, int S>
-__global__ __launch_bounds__(256) void k_qkv_epi(QkvEpi e) {
-  const int m = blockIdx.y;
-  const int u = blockIdx.x * 256 + threadIdx.x;
-  const int hd = e.hd, half = hd >> 1;
-  const int nq = e.H * hd, nk = e.Hkv * hd;
-  const int npair = (e.H + e.Hkv) * half;
-  if (u >= npair + nk) return;
-  const int pos = e.pos[m];
-  if (u < npair) {
-    const int hh = u / half, i = u - hh * half;
-    const int col = hh * hd + i;
-    const float x1 = sum_pieces<S>(e.part, e.sp, e.rows_pad, e.N, m, col);
-    const float x2 = sum_pieces<S>(e.part, e.sp, e.rows_pad, e.N, m, col + half);
-    const float2 cs = e.rope[(size_t)pos * half + i];
-    const float y1 = x1 * cs.x - x2 * cs.y;
-    const float y2 = x1 * cs.y + x2 * cs.x;
-    if (hh < e.H) {
-      T* q = (T*)e.q + (size_t)m * nq + hh * hd;
-      st_f(q + i, y1);
-      st_f(q + i + half, y2);
-    } else {
-      const int kvh = hh - e.H;
-      T* kd = (T*)e.kdst;
-      T* dst = e.dest == QKV_TO_BLOCK ? kd + (size_t)m * nk + kvh * hd
-                                      : kd + ((size_t)kvh * e.ld_ctx + pos) * hd;
-      st_f(dst + i, y1);
-      st_f(dst + i + half, y2);
-    }
-  } else {
-    const int vi = u - npair;
-    const float v = sum_pieces<S>(e.part, e.sp, e.rows_pad, e.N, m, nq + nk + vi);
-    const int kvh = vi / hd, i = vi - kvh * hd;
-    T* vd = (T*)e.vdst;
-    T* dst = e.dest == QKV_TO_BLOCK ? vd + (size_t)m * nk + vi
-                                    : vd + ((size_t)kvh * e.ld_ctx + pos) * hd + i;
-    st_f(dst, v);
-  }
-}
-
-// x[m] += sum of the pieces (in K order); then
-// h[m] = x[m] / sqrt(mean(x^2) + eps) * g: the residual add fused with the
-// next RMSNorm.  One workgroup of d/NC threads per row; thread t owns columns
-// t + j*blockDim; the sum of squares is reduced in a fixed order (within a
-// wave by xor-shuffles, then across waves in wave order).
-template <typename T, int S, int NC>
-__global__ __launch_bounds__(1024) void k_resid_norm(const float* __restrict__ part, SplitPlan sp,
-                                                     int rows_pad,
-                                                     int d, float* __restrict__ x,
-                                                     const T* __restrict__ g, T* __restrict__ h,
-                                                     float eps) {
-  __shared__ float red[16];
-  const int m = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
-  float* xr = x + (size_t)m * d;
-  float v[NC];
-#pragma unroll
-  for (int j = 0; j < NC; ++j) v[j] = sum_pieces<S>(part, sp, rows_pad, d, m, tid + j * nt);
-  float ss = 0.f;
-#pragma unroll
-  for (int j = 0; j < NC; ++j) {
-    v[j] = xr[tid + j * nt] + v[j];
-    xr[tid + j * nt] = v[j];
-    ss = fmaf(v[j], v[j], ss);
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
-  if ((tid & 63) == 0) red[tid >> 6] = ss;
-  __syncthreads();
-  float tot = 0.f;
-  for (int w = 0; w < (nt >> 6); ++w) tot += red[w];
-  const float rs = 1.0f / sqrtf(tot / (float)d + eps);
-  T* hr = h + (size_t)m * d;
-#pragma unroll
-  for (int j = 0; j < NC; ++j) st_f(hr + tid + j * nt, v[j] * rs * ld_f(g + tid + j * nt));
-}
-
-template <int S>
-__global__ __launch_bounds__(256) void k_sum_epi(const float* part, SplitPlan sp, int rows_pad,
-                                                 int N, float* y) {
-  const int m = blockIdx.y;
-  const int n = blockIdx.x * 256 + threadIdx.x;
-  if (n >= N) return;
-  y[(size_t)m * N + n] = sum_pieces<S>(part, sp, rows_pad, N, m, n);
-}
-
-template <typename T, int S>
-__global__ __launch_bounds__(256) void k_silu_epi(const float* part, SplitPlan sp, int rows_pad,
-                                                  int F, T* act) {
-  const int m = blockIdx.y;
-  const int f = blockIdx.x * 256 + threadIdx.x;
-  if (f >= F) return;
-  const float gt = sum_pieces<S>(part, sp, rows_pad, 2 * F, m, f);
-  const float up = sum_pieces<S>(part, sp, rows_pad, 2 * F, m, F + f);
-  const float sg = gt / (1.0f + expf(-gt));
-  st_f(act + (size_t)m * F + f, sg * up);
-}
-
 // dst block (stripe s, chunk c): element (j, lane, e) = W[16s + lane%16][64c + 32j + 8(lane/16) + e]
 __global__ __launch_bounds__(128) void k_pack_bf16(const bf16_t* __restrict__ src, int N, int K,
                                                    bf16_t* __restrict__ dst) {
@@ -754,78 +629,5 @@ hipError_t launch_gemm(const GemmDesc& g, int dtype, hipStream_t st) {
     case 7: hipLaunchKernelGGL(k_gemm4<7>, grid, b4, 0, st, g); break;
     default: hipLaunchKernelGGL(k_gemm4<8>, grid, b4, 0, st, g); break;
   }
-  return hipGetLastError();
-}
-
-hipError_t launch_qkv_epi(const QkvEpi& e, int dtype, hipStream_t st) {
-  const int units = (e.H + e.Hkv) * (e.hd / 2) + e.Hkv * e.hd;
-  dim3 grid((units + 255) / 256, e.rows);
-#define LA_QKV(S_)                                                              \
-  if (dtype == LA_BF16)                                                         \
-    hipLaunchKernelGGL((k_qkv_epi<bf16_t, S_>), grid, dim3(256), 0, st, e);     \
-  else                                                                          \
-    hipLaunchKernelGGL((k_qkv_epi<float, S_>), grid, dim3(256), 0, st, e);
-  LA_SPLIT_DISPATCH(e.sp.np, LA_QKV)
-#undef LA_QKV
-  return hipGetLastError();
-}
-
-// columns per thread for a row of d values in one workgroup (<= 1024 threads)
-static int norm_nc(int d) {
-  for (int nc = 1; nc <= 16; ++nc)
-    if (d % nc == 0 && d / nc <= 1024 && (d / nc) % 64 == 0) return nc;
-  return 0;
-}
-
-hipError_t launch_resid_norm(const float* part, const SplitPlan& sp, int rows_pad, int d,
-                             int rows, float* x, const void* g, void* h, float eps, int dtype,
-                             hipStream_t st) {
-  const int nc = norm_nc(d);
-  if (!nc) return hipErrorInvalidValue;
-  const dim3 blk(d / nc);
-#define LA_RN2(S_, NC_)                                                                        \
-  if (dtype == LA_BF16)                                                                        \
-    hipLaunchKernelGGL((k_resid_norm<bf16_t, S_, NC_>), dim3(rows), blk, 0, st, part, sp,      \
-                       rows_pad, d, x, (const bf16_t*)g, (bf16_t*)h, eps);                     \
-  else                                                                                         \
-    hipLaunchKernelGGL((k_resid_norm<float, S_, NC_>), dim3(rows), blk, 0, st, part, sp,       \
-                       rows_pad, d, x, (const float*)g, (float*)h, eps);
-#define LA_RN(S_)                                                       \
-  switch (nc) {                                                         \
-    case 1: LA_RN2(S_, 1) break;                                        \
-    case 2: LA_RN2(S_, 2) break;                                        \
-    case 4: LA_RN2(S_, 4) break;                                        \
-    case 5: LA_RN2(S_, 5) break;                                        \
-    case 8: LA_RN2(S_, 8) break;                                        \
-    case 16: LA_RN2(S_, 16) break;                                      \
-    default: return hipErrorInvalidValue;                               \
-  }
-  LA_SPLIT_DISPATCH(sp.np, LA_RN)
-#undef LA_RN
-#undef LA_RN2
-  return hipGetLastError();
-}
-
-hipError_t launch_sum_epi(const float* part, const SplitPlan& sp, int rows_pad, int N, int rows,
-                          float* y, hipStream_t st) {
-#define LA_SE(S_)                                                                           \
-  hipLaunchKernelGGL((k_sum_epi<S_>), dim3((N + 255) / 256, rows), dim3(256), 0, st, part, sp, \
-                     rows_pad, N, y);
-  LA_SPLIT_DISPATCH(sp.np, LA_SE)
-#undef LA_SE
-  return hipGetLastError();
-}
-
-hipError_t launch_silu_epi(const float* part, const SplitPlan& sp, int rows_pad, int F, int rows,
-                           void* act, int dtype, hipStream_t st) {
-#define LA_SI(S_)                                                                              \
-  if (dtype == LA_BF16)                                                                        \
-    hipLaunchKernelGGL((k_silu_epi<bf16_t, S_>), dim3((F + 255) / 256, rows), dim3(256), 0, st, \
-                       part, sp, rows_pad, F, (bf16_t*)act);                                   \
-  else                                                                                         \
-    hipLaunchKernelGGL((k_silu_epi<float, S_>), dim3((F + 255) / 256, rows), dim3(256), 0, st,  \
-                       part, sp, rows_pad, F, (float*)act);
-  LA_SPLIT_DISPATCH(sp.np, LA_SI)
-#undef LA_SI
   return hipGetLastError();
 }

@@ -67,6 +67,8 @@ struct RowLayout {
 // The pieces a column block is cut into are summed in K order by the
 // epilogue.  The plan depends on (N, K) only, never on the row count, so a
 // row gets the same sums at any M.
+constexpr int GEMM_NWG = 128;  // output columns of one GEMM column block
+
 struct SplitPlan {
   int nch;   // K / 64
   int nblk;  // column blocks of 128
@@ -165,17 +167,22 @@ hipError_t launch_attention(const AttnDesc& a, int dtype, hipStream_t st);
 // Whether the MFMA kernel takes the shared prefix (bf16, head_dim 128).
 int attn_uses_mfma(int dtype, int hd);
 // The shared prefix of a row is split into chunks on a fixed partition of
-// absolute positions (128 wide below 1024, 256 wide below 4096, 512 wide
-// after), so a row's arithmetic depends on its position only, never on the
-// session's context capacity.
+// absolute positions (64 wide below 512, 128 below 1024, 256 below 4096, 512
+// after: short prefixes spread over more workgroups, long ones keep the
+// number of partials down), so a row's arithmetic depends on its position
+// only, never on the session's context capacity.
 __host__ __device__ inline int attn_chunk_start(int s) {
-  return s <= 8 ? 128 * s : s <= 20 ? 1024 + 256 * (s - 8) : 4096 + 512 * (s - 20);
+  return s <= 8 ? 64 * s
+       : s <= 12 ? 512 + 128 * (s - 8)
+       : s <= 24 ? 1024 + 256 * (s - 12)
+                 : 4096 + 512 * (s - 24);
 }
 __host__ __device__ inline int attn_nchunks(int L) {  // chunks meeting [0, L)
   if (L <= 0) return 0;
-  if (L <= 1024) return (L + 127) / 128;
-  if (L <= 4096) return 8 + (L - 1024 + 255) / 256;
-  return 20 + (L - 4096 + 511) / 512;
+  if (L <= 512) return (L + 63) / 64;
+  if (L <= 1024) return 8 + (L - 512 + 127) / 128;
+  if (L <= 4096) return 12 + (L - 1024 + 255) / 256;
+  return 24 + (L - 4096 + 511) / 512;
 }
 size_t attn_part_floats(int nsplit, int rows, int H, int hd);
 
