@@ -7,7 +7,7 @@
 // key at each position 0..pos(row): committed positions < P come from the KV
 // cache, and position P+j comes from the block row `chain_row(row, j)`.
 //
-// Each row's keys are visited in absolute-position tiles of 64 with a fixed
+// Each row's keys are visited in absolute-position tiles with a fixed
 // summation order, so a row's result depends only on the keys it sees, not on
 // whether they sit in the cache or in the block, nor on the other rows: the
 // verification row that reproduces an autoregressive step gets the bits of
@@ -99,15 +99,18 @@ __device__ __forceinline__ float dot_q(const float* qs, const float* k) {
 }
 
 constexpr int AT = 64;  // attention tile (positions)
+constexpr int BT = 16;  // granularity of the MFMA part's end
 
-// End of the MFMA part of a row's keys (a multiple of AT): at least D keys
+// End of the MFMA part of a row's keys (a multiple of BT): at least D keys
 // before the row's own position stay in the per-row part, and never a block
 // position (>= P).  A verification row at P+i (i <= D) and the
-// autoregressive query at the same position get the same split.
+// autoregressive query at the same position get the same split.  The MFMA
+// kernel masks per key, so the per-row part is at most D + BT keys long for
+// a verification row.
 __device__ __forceinline__ int bulk_end(int pos, int P, int D) {
   int f = pos - D;
-  f = f < 0 ? 0 : (f / AT) * AT;
-  const int pf = (P / AT) * AT;
+  f = f < 0 ? 0 : (f / BT) * BT;
+  const int pf = (P / BT) * BT;
   return f < pf ? f : pf;
 }
 
@@ -365,18 +368,32 @@ __global__ __launch_bounds__(256) void k_attn_bulk(AttnDesc a) {
 
   // K [key][dim] and V^T [dim][key] of a 64-position tile: each thread holds
   // 32 dims of one key of K and 16 dims of a key pair of V, fetched one tile
-  // ahead so the loads of tile t+1 overlap the arithmetic of tile t
+  // ahead so the loads of tile t+1 overlap the arithmetic of tile t.  Keys
+  // at or past tend (past every row's MFMA part, possibly never written)
+  // are staged as zeros: masked rows then add exactly 0 * 0.
   const int fkey = tid >> 2, fseg = tid & 3;  // K: 32 dims per thread
   const int fkp = tid & 31, fvs = tid >> 5;   // V: key pair, 16-dim segment
   u32x4_t kf[4];
   U4 va0, va1, vb0, vb1;
+  const u32x4_t z4 = u32x4_t{0u, 0u, 0u, 0u};
   auto fetch = [&](int t0) __attribute__((always_inline)) {
-    const u32x4_t* src = (const u32x4_t*)(kc + (size_t)(t0 + fkey) * 128 + fseg * 32);
+    // addresses clamped to key tend-1 (a tile may reach past the cache's
+    // capacity); the loaded words of such keys are replaced by zeros
+    const int k0 = t0 + fkey, v0k = t0 + 2 * fkp;
+    const int kl = min(k0, tend - 1), v0l = min(v0k, tend - 1), v1l = min(v0k + 1, tend - 1);
+    const u32x4_t* src = (const u32x4_t*)(kc + (size_t)kl * 128 + fseg * 32);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) kf[j] = src[j];
-    const u32x4_t* v0 = (const u32x4_t*)(vc + (size_t)(t0 + 2 * fkp) * 128 + fvs * 16);
-    const u32x4_t* v1 = (const u32x4_t*)(vc + (size_t)(t0 + 2 * fkp + 1) * 128 + fvs * 16);
-    va0.u = v0[0]; va1.u = v0[1]; vb0.u = v1[0]; vb1.u = v1[1];
+    for (int j = 0; j < 4; ++j) {
+      const u32x4_t w = src[j];
+      kf[j] = k0 < tend ? w : z4;
+    }
+    const u32x4_t* v0 = (const u32x4_t*)(vc + (size_t)v0l * 128 + fvs * 16);
+    const u32x4_t* v1 = (const u32x4_t*)(vc + (size_t)v1l * 128 + fvs * 16);
+    const u32x4_t a0 = v0[0], a1 = v0[1], b0 = v1[0], b1 = v1[1];
+    va0.u = v0k < tend ? a0 : z4;
+    va1.u = v0k < tend ? a1 : z4;
+    vb0.u = v0k + 1 < tend ? b0 : z4;
+    vb1.u = v0k + 1 < tend ? b1 : z4;
   };
   if (s0 < tend) fetch(s0);
   for (int t0 = s0; t0 < tend; t0 += AT) {
@@ -394,9 +411,10 @@ __global__ __launch_bounds__(256) void k_attn_bulk(AttnDesc a) {
 #pragma unroll
     for (int gi = 0; gi < 2; ++gi) {
       if (!gon[gi]) continue;
-      const bool valid = t0 + AT <= F[gi];
+      // keys [t0, F) of the tile are this lane's row's (F a multiple of BT)
+      const int nv = F[gi] - t0;
       // skip the group when the tile is past every one of its rows
-      const bool any = __any(valid);
+      const bool any = __any(nv > 0);
       if (!any) continue;
       f32x4_t st[4];
 #pragma unroll
@@ -414,7 +432,7 @@ __global__ __launch_bounds__(256) void k_attn_bulk(AttnDesc a) {
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float sv = valid ? st[kb][e] * scale : -INFINITY;
+          const float sv = kb * 16 + 4 * q4 + e < nv ? st[kb][e] * scale : -INFINITY;
           st[kb][e] = sv;
           mt = fmaxf(mt, sv);
         }
@@ -432,7 +450,7 @@ __global__ __launch_bounds__(256) void k_attn_bulk(AttnDesc a) {
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float pv = valid ? expf(st[kb][e] - m_new) : 0.f;
+          const float pv = kb * 16 + 4 * q4 + e < nv ? expf(st[kb][e] - m_new) : 0.f;
           ls += pv;
           const uint16_t hb = f2bf(pv);
           pa[kb >> 1].h[(kb & 1) * 4 + e] = hb;
