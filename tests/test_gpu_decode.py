@@ -15,6 +15,7 @@ import pytest
 torch = pytest.importorskip("torch")
 
 import synth
+from exact_decoding_amd import binding as B
 from exact_decoding_amd.runtime import Model
 from oracle import lookahead as la
 from oracle.model import OracleModel
@@ -141,4 +142,74 @@ def test_bf16_exact_whatever_the_context_capacity():
     ar_ses.close()
     gm.close()
     assert len(la_toks) == n_new
+    assert la_toks == ar_toks
+
+
+@pytest.mark.parametrize("N,W,G,plen,prompt_ref", [
+    (2, 1, 1, 16, True),     # shortest n-grams
+    (2, 4, 0, 16, False),    # no verification branch
+    (3, 0, 4, 16, True),     # no lookahead branch: candidates from the prompt only
+    (16, 2, 2, 16, True),    # longest n-grams (LA_MAX_N)
+    (4, 3, 3, 1, False),     # one-token prompt: no prefill forward
+    (4, 3, 3, 2, True),      # prompt shorter than an n-gram: nothing to seed
+    (5, 0, 0, 8, False),     # M = 1: the step degenerates to AR
+])
+def test_tiny_edge_configs_match_oracle(tiny, N, W, G, plen, prompt_ref):
+    """Degenerate shapes of the method against the oracle: every token, the
+    tokens of each step and every pool counter."""
+    s, w, gm, om = tiny
+    n_new = 24
+    prompt = synth.prompt_motif(s.vocab, seed=1)[:plen]
+    win = synth.gen_window(N, W, s.vocab, seed=2)
+    print(f"tiny fp32 N={N} W={W} G={G} prompt={plen} ref={prompt_ref}", flush=True)
+    ref = la.lookahead(om, prompt, N, W, G, n_new, win, prompt_ref=prompt_ref)
+    assert ref.tokens == la.greedy_ar(om, prompt, n_new).tokens
+    ses = gm.session(prompt, N, W, G, n_new, window=win if W else None, prompt_ref=prompt_ref)
+    ses.decode()
+    st = ses.stats()
+    assert ses.tokens == ref.tokens
+    assert ses.per_step == ref.emitted
+    assert st["steps"] == ref.steps
+    assert [st["accept_hist"][j] for j in range(N)] == [ref.accepted.count(j) for j in range(N)]
+    assert st["inserts"] == ref.pool.inserts and st["dup_skips"] == ref.pool.dup_skips
+    assert st["evictions"] == ref.pool.evictions
+    assert st["pool_ngrams"] == ref.pool.n_ngrams() and st["pool_keys_nonempty"] == ref.pool.n_keys()
+    ses.close()
+
+
+def test_context_full_is_reported(tiny):
+    """A step that would write past max_ctx is refused with LA_ECTX before any
+    device work; the tokens emitted until then are the AR stream's prefix."""
+    s, w, gm, om = tiny
+    N, W, G = 3, 4, 4
+    prompt = synth.prompt_motif(s.vocab, seed=1)
+    max_ctx = len(prompt) + 12
+    ses = gm.session(prompt, N, W, G, 64, window=synth.gen_window(N, W, s.vocab, seed=2),
+                     max_ctx=max_ctx)
+    with pytest.raises(B.LaError) as ei:
+        while not ses.done:
+            ses.step()
+    assert ei.value.code == B.LA_ECTX
+    ar = la.greedy_ar(om, prompt, len(ses.tokens))
+    assert len(ses.tokens) >= 1 and ses.tokens == ar.tokens
+    ses.close()
+
+
+def test_bf16_near_maximum_rows_bit_exact():
+    """M = 1 + (66 + 66) * 15 = 1981 rows (the limit is 2048): sixteen 128-row
+    GEMM tiles, chains up to N + W - 1 = 81 keys long, and still the AR stream
+    bit for bit."""
+    s = synth.SHAPES["small_bf16"]
+    gm = Model(s, synth.gen_weights(s, 0))
+    N, W, G, n_new = 16, 66, 66, 24
+    prompt = synth.prompt_zipf_spans(s.vocab, length=64, seed=1)
+    la_ses = gm.session(prompt, N, W, G, n_new, window=synth.gen_window(N, W, s.vocab, seed=2),
+                        prompt_ref=True)
+    assert la_ses.rows == 1981
+    la_toks = la_ses.decode()
+    la_ses.close()
+    ar_ses = gm.session(prompt, N, W, G, n_new, ar=True)
+    ar_toks = ar_ses.decode()
+    ar_ses.close()
+    gm.close()
     assert la_toks == ar_toks
