@@ -48,6 +48,10 @@ def parse():
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--cpu-tokens", type=int, default=48)
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the benchmark line: step time against the row count "
+                         "M over a grid of (N, W = G), one JSON line per configuration")
+    ap.add_argument("--sweep-steps", type=int, default=32)
     ap.add_argument("--calibrate", action="store_true",
                     help="first run a 1 GiB HBM read (la_probe_read) and a 1 GiB fill, "
                          "the known-size kernels that scale the PMC byte counters")
@@ -154,6 +158,51 @@ def cpu_baseline(shape, weights, prompt, n_tokens):
                       f"weights {'decoded once' if om.keep else 'decoded per call'}"}
 
 
+SWEEP_N = (3, 5, 7)
+SWEEP_W = (1, 2, 4, 7, 10, 15, 20, 30)
+
+
+def sweep(args, model, shape, prompt):
+    """Step time of the engine against M = 1 + (W + G)(N - 1) (G = W), next to
+    the AR step: the ratio is the compression S a model must reach for the
+    lookahead step to pay off at that configuration on this GPU."""
+    import synth
+    K = args.sweep_steps
+
+    def time_steps(N, W, G, ar):
+        ses = model.session(prompt, N, W, G, K + 8, ar=ar,
+                            window=None if ar else synth.gen_window(N, W, shape.vocab, seed=2),
+                            prompt_ref=not ar)
+        for _ in range(4):
+            ses.step()
+        n0, s0 = len(ses.tokens), len(ses.per_step)
+        import torch
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(K):
+            if ses.done:
+                break
+            ses.step()
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        steps = len(ses.per_step) - s0
+        S = (len(ses.tokens) - n0) / max(steps, 1)
+        rows = ses.rows
+        ses.close()
+        return dt * 1e3 / max(steps, 1), S, rows
+
+    ar_ms, _, _ = time_steps(5, 0, 0, True)
+    log(f"[sweep] AR step {ar_ms:.3f} ms")
+    for N in SWEEP_N:
+        for W in SWEEP_W:
+            if 1 + 2 * W * (N - 1) > 2048:
+                continue
+            ms, S, rows = time_steps(N, W, W, False)
+            print(json.dumps({"shape": shape.name, "N": N, "W": W, "G": W, "M": rows,
+                              "step_ms": ms, "ar_step_ms": ar_ms, "break_even_S": ms / ar_ms,
+                              "measured_S": S}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -186,6 +235,9 @@ def main():
     prompt = synth.prompt_zipf_spans(shape.vocab, length=args.prompt_len, seed=1)
     window = synth.gen_window(N, W, shape.vocab, seed=2)
     graph = not args.no_graph
+    if args.sweep:
+        sweep(args, model, shape, prompt)
+        return
     sync = torch.cuda.synchronize
 
     def la_session():
