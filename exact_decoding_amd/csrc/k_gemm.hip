@@ -193,8 +193,10 @@ __global__ __launch_bounds__(320) void k_gemm_bf16(GemmDesc g) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const bf16_t* p = wptr(t, tt);
-      dst[tt][0] = *(const u32x4_t*)p;
-      dst[tt][1] = *(const u32x4_t*)(p + 512);
+      // streaming hint: each weight line is used once; measured 7-10% faster
+      // at one row tile (it did not help the multi-tile kernel)
+      dst[tt][0] = __builtin_nontemporal_load((const u32x4_t*)p);
+      dst[tt][1] = __builtin_nontemporal_load((const u32x4_t*)(p + 512));
     }
   };
   // A-fragment offsets (bf16) in a stage: row i*16 + r, k 32j + 8q .. +8
