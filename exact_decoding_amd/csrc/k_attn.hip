@@ -66,38 +66,6 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// dot(q, k) over HD: four interleaved partial sums (dimension d goes to
-// partial d mod 4, each partial in increasing d), added as (p0+p1)+(p2+p3).
-template <int HD>
-__device__ __forceinline__ float dot_q(const float* qs, const bf16_t* k) {
-  float a[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int d0 = 0; d0 < HD; d0 += 8) {
-    const u32x4_t u = *(const u32x4_t*)(k + d0);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      a[(2 * e) & 3] = fmaf(qs[d0 + 2 * e], __uint_as_float(w[e] << 16), a[(2 * e) & 3]);
-      a[(2 * e + 1) & 3] =
-          fmaf(qs[d0 + 2 * e + 1], __uint_as_float(w[e] & 0xFFFF0000u), a[(2 * e + 1) & 3]);
-    }
-  }
-  return (a[0] + a[1]) + (a[2] + a[3]);
-}
-template <int HD>
-__device__ __forceinline__ float dot_q(const float* qs, const float* k) {
-  float a[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int d0 = 0; d0 < HD; d0 += 4) {
-    const float4 u = *(const float4*)(k + d0);
-    a[0] = fmaf(qs[d0], u.x, a[0]);
-    a[1] = fmaf(qs[d0 + 1], u.y, a[1]);
-    a[2] = fmaf(qs[d0 + 2], u.z, a[2]);
-    a[3] = fmaf(qs[d0 + 3], u.w, a[3]);
-  }
-  return (a[0] + a[1]) + (a[2] + a[3]);
-}
-
 constexpr int AT = 64;  // attention tile (positions)
 constexpr int BT = 16;  // granularity of the MFMA part's end
 
@@ -118,16 +86,25 @@ __device__ __forceinline__ int row_pos(const AttnDesc& a, int r, int Pc) {
   return a.pos ? a.pos[r] : Pc + row_offset(r, a.lay);
 }
 
-// Per-row part: one wave per (head, row) over positions [F, pos] in
-// absolute-position tiles of 64 (keys from the cache below P, from the
-// block chain above).  Lane j of a tile scores the key at position 64t + j;
-// lanes own output dimensions lane, lane+64 for the P.V sum.  Writes the
-// normalised output when there is no MFMA part, else (m, l, o) partials.
+// Per-row part: one wave per (head, row) over positions [F, pos] in tiles of
+// TT = 32 positions starting at F (keys from the cache below P, from the
+// block chain above); F is a function of pos, so a tile, and the place of
+// each key in it, depend only on the row's position.  With D + BT <= TT the
+// part is a single tile.  Key slot j of a tile (position base + j) is held by
+// the lane pair 2j, 2j+1, each lane with half of the key's dimensions; the
+// pair adds its two half dot products low half first.  For the P.V sum lanes
+// own output dimensions.  Writes the normalised output after merging the MFMA
+// kernel's (m, l, o) partials of [0, F) in chunk order.
+constexpr int TT = 32;  // per-row tile (positions)
+
+// half of dot(q, k): dimensions [h0, h0 + HD/2), four interleaved partial
+// sums (dimension d to partial d mod 4, each in increasing d) added as
+// (p0+p1)+(p2+p3)
 template <int HD>
-__device__ __forceinline__ float dot_r(const float* qs, const u32x4_t (&k)[HD / 8], bf16_t) {
+__device__ __forceinline__ float dot_half(const float* qs, const u32x4_t (&k)[HD / 16], bf16_t) {
   float a[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int c = 0; c < HD / 8; ++c) {
+  for (int c = 0; c < HD / 16; ++c) {
     const uint32_t w[4] = {k[c].x, k[c].y, k[c].z, k[c].w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -139,10 +116,10 @@ __device__ __forceinline__ float dot_r(const float* qs, const u32x4_t (&k)[HD / 
   return (a[0] + a[1]) + (a[2] + a[3]);
 }
 template <int HD>
-__device__ __forceinline__ float dot_r(const float* qs, const u32x4_t (&k)[HD / 4], float) {
+__device__ __forceinline__ float dot_half(const float* qs, const u32x4_t (&k)[HD / 8], float) {
   float a[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int c = 0; c < HD / 4; ++c) {
+  for (int c = 0; c < HD / 8; ++c) {
     a[0] = fmaf(qs[4 * c], __uint_as_float(k[c].x), a[0]);
     a[1] = fmaf(qs[4 * c + 1], __uint_as_float(k[c].y), a[1]);
     a[2] = fmaf(qs[4 * c + 2], __uint_as_float(k[c].z), a[2]);
@@ -154,12 +131,15 @@ __device__ __forceinline__ float dot_r(const float* qs, const u32x4_t (&k)[HD / 
 template <typename T, int HD>
 __global__ __launch_bounds__(64) void k_attn_tail(AttnDesc a) {
   constexpr int NV = HD * (int)sizeof(T) / 16;       // 16-byte words per K / V row
+  constexpr int NH = NV / 2;                         // words per half row (one lane)
   constexpr int DPL = HD >= 64 ? HD / 64 : 1;        // output dims per lane (contiguous)
   constexpr int VSTRIDE = HD + 16 / (int)sizeof(T);  // padded LDS row of V
+  static_assert(NV % 2 == 0, "a lane holds half a row");
   __shared__ float qs[HD];
-  __shared__ float ps[AT];
-  __shared__ __align__(16) T vs[AT * VSTRIDE];
+  __shared__ float ps[TT];
+  __shared__ __align__(16) T vs[TT * VSTRIDE];
   const int h = blockIdx.x, r = blockIdx.y, lane = threadIdx.x;
+  const int slot = lane >> 1, half = lane & 1;
   const int kvh = h * a.Hkv / a.H;
   const int Pc = a.Pdev ? *a.Pdev : a.P_host;
   const int pos = row_pos(a, r, Pc);
@@ -167,10 +147,10 @@ __global__ __launch_bounds__(64) void k_attn_tail(AttnDesc a) {
   const int F = a.mfma ? bulk_end(pos, P, a.D) : 0;
   const int ldb = a.Hkv * HD;
   const T* q = (const T*)a.q + (size_t)r * a.H * HD + h * HD;
-  const T* kc = (const T*)a.kc + (size_t)kvh * a.ld_ctx * HD;
-  const T* vc = (const T*)a.vc + (size_t)kvh * a.ld_ctx * HD;
-  const T* kb = (const T*)a.kb + kvh * HD;
-  const T* vb = (const T*)a.vb + kvh * HD;
+  const T* kc = (const T*)a.kc + (size_t)kvh * a.ld_ctx * HD + half * (HD / 2);
+  const T* vc = (const T*)a.vc + (size_t)kvh * a.ld_ctx * HD + half * (HD / 2);
+  const T* kb = (const T*)a.kb + kvh * HD + half * (HD / 2);
+  const T* vb = (const T*)a.vb + kvh * HD + half * (HD / 2);
   const float scale = 1.0f / sqrtf((float)HD);
   const int d0 = lane * DPL;
   const bool down = d0 < HD;
@@ -180,47 +160,52 @@ __global__ __launch_bounds__(64) void k_attn_tail(AttnDesc a) {
 #pragma unroll
   for (int j = 0; j < DPL; ++j) o[j] = 0.f;
 
-  // the MFMA kernel's partials of the first NPRE chunks of [0, F), loaded
-  // now so their latency overlaps the tile loads below
-  constexpr int NPRE = 4;
+  // the MFMA kernel's partials of the chunks of [0, F), merged in chunk
+  // order; NPRE of them are in flight at a time, the first NPRE loaded now so
+  // their latency overlaps the tile below
+  constexpr int NPRE = 8;
+  const int nch = a.mfma ? attn_nchunks(F) : 0;
   float pm[NPRE], pl[NPRE], po[NPRE][DPL];
-#pragma unroll
-  for (int sp = 0; sp < NPRE; ++sp) {
-    if (a.mfma && attn_chunk_start(sp) < F) {
+  auto load_part = [&](int sp, int i) __attribute__((always_inline)) {
+    if (sp < nch) {
       const size_t pb = ((size_t)sp * a.rows + r) * a.H + h;
-      pm[sp] = a.part_ml[pb * 2];
-      pl[sp] = a.part_ml[pb * 2 + 1];
+      pm[i] = a.part_ml[pb * 2];
+      pl[i] = a.part_ml[pb * 2 + 1];
 #pragma unroll
-      for (int j = 0; j < DPL; ++j) po[sp][j] = down ? a.part_o[pb * HD + d0 + j] : 0.f;
+      for (int j = 0; j < DPL; ++j) po[i][j] = down ? a.part_o[pb * HD + d0 + j] : 0.f;
     }
-  }
+  };
+#pragma unroll
+  for (int i = 0; i < NPRE; ++i) load_part(i, i);
+  for (int i = lane; i < HD; i += 64) qs[i] = ld_f(q + i);
 
-  // tiles of 64 absolute positions over [F, pos]; lane j holds key 64t + j
-  for (int t = F / AT; t <= pos / AT; ++t) {
-    const int p = t * AT + lane;
-    const bool on = p >= F && p <= pos;
-    u32x4_t kr[NV], vr[NV];
+  // tiles of TT positions over [F, pos]
+  for (int base = F; base <= pos; base += TT) {
+    const int p = base + slot;
+    const bool on = p <= pos;
+    u32x4_t kr[NH], vr[NH];
     if (on) {
       const int src = p < P ? -1 : chain_row(r, p - P, a.lay);
       const u32x4_t* kp = (const u32x4_t*)(src < 0 ? kc + (size_t)p * HD : kb + (size_t)src * ldb);
       const u32x4_t* vp = (const u32x4_t*)(src < 0 ? vc + (size_t)p * HD : vb + (size_t)src * ldb);
 #pragma unroll
-      for (int e = 0; e < NV; ++e) kr[e] = kp[e];
+      for (int e = 0; e < NH; ++e) kr[e] = kp[e];
 #pragma unroll
-      for (int e = 0; e < NV; ++e) vr[e] = vp[e];
+      for (int e = 0; e < NH; ++e) vr[e] = vp[e];
     }
-    if (t == F / AT)
-      for (int i = lane; i < HD; i += 64) qs[i] = ld_f(q + i);
     if (on) {
 #pragma unroll
-      for (int e = 0; e < NV; ++e) *(u32x4_t*)((char*)(vs + lane * VSTRIDE) + 16 * e) = vr[e];
+      for (int e = 0; e < NH; ++e)
+        *(u32x4_t*)((char*)(vs + slot * VSTRIDE + half * (HD / 2)) + 16 * e) = vr[e];
     }
     __syncthreads();
-    const float sc = on ? dot_r<HD>(qs, kr, T()) * scale : -INFINITY;
+    const float mine = on ? dot_half<HD>(qs + half * (HD / 2), kr, T()) : 0.f;
+    const float other = __shfl_xor(mine, 1, 64);
+    const float sc = on ? ((half ? other : mine) + (half ? mine : other)) * scale : -INFINITY;
     const float mp = wave_max(sc);
     const float pv = on ? expf(sc - mp) : 0.f;
-    ps[lane] = pv;
-    const float lp = wave_sum(pv);
+    if (!half) ps[slot] = pv;
+    const float lp = wave_sum(half ? 0.f : pv);
     __syncthreads();
     // P.V over this tile: key j goes to partial j mod 4
     float acc[4][DPL];
@@ -229,9 +214,8 @@ __global__ __launch_bounds__(64) void k_attn_tail(AttnDesc a) {
 #pragma unroll
       for (int j = 0; j < DPL; ++j) acc[u][j] = 0.f;
     if (down) {
-      const int j0 = F > t * AT ? F - t * AT : 0;
-      const int n = min(AT, pos - t * AT + 1);
-      for (int jj = j0; jj < n; jj += 4) {
+      const int n = min(TT, pos - base + 1);
+      for (int jj = 0; jj < n; jj += 4) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           if (jj + u < n) {
@@ -268,15 +252,14 @@ __global__ __launch_bounds__(64) void k_attn_tail(AttnDesc a) {
       for (int j = 0; j < DPL; ++j) oo[j] = oo[j] * ca + os[j] * cb;
     m = mn;
   };
+  for (int sp0 = 0; sp0 < nch; sp0 += NPRE) {
 #pragma unroll
-  for (int sp = 0; sp < NPRE; ++sp)
-    if (a.mfma && attn_chunk_start(sp) < F) merge(pm[sp], pl[sp], po[sp]);
-  for (int sp = NPRE; a.mfma && attn_chunk_start(sp) < F; ++sp) {
-    const size_t pb = ((size_t)sp * a.rows + r) * a.H + h;
-    float os[DPL];
-#pragma unroll
-    for (int j = 0; j < DPL; ++j) os[j] = down ? a.part_o[pb * HD + d0 + j] : 0.f;
-    merge(a.part_ml[pb * 2], a.part_ml[pb * 2 + 1], os);
+    for (int i = 0; i < NPRE; ++i) {
+      if (sp0 + i < nch) {
+        merge(pm[i], pl[i], po[i]);
+        load_part(sp0 + i + NPRE, i);
+      }
+    }
   }
   {
     const float mn = fmaxf(m, m_run);
@@ -365,6 +348,9 @@ __global__ __launch_bounds__(256) void k_attn_bulk(AttnDesc a) {
   atomicMax(&s_fmax, max(F[0], F[1]));
   __syncthreads();
   tend = min(attn_chunk_start(split + 1), s_fmax);
+  // no row of the workgroup has keys in this chunk: the per-row kernel reads
+  // none of its partials
+  if (tend <= s0) return;
 
   // K [key][dim] and V^T [dim][key] of a 64-position tile: each thread holds
   // 32 dims of one key of K and 16 dims of a key pair of V, fetched one tile

@@ -153,7 +153,7 @@ struct AttnDesc {
   RowLayout lay;
   // Split of each row's keys: the committed tiles [0, F) go through the MFMA
   // kernel in the chunks of attn_chunk_start, [F, pos] through the per-row
-  // kernel; F = min(floor((pos - D) / 64) * 64, floor(P / 64) * 64).
+  // kernel; F = min(floor((pos - D) / 16) * 16, floor(P / 16) * 16).
   // mfma == 0: no MFMA part (F = 0).
   int D;
   int mfma;
