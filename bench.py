@@ -191,16 +191,26 @@ def sweep(args, model, shape, prompt):
         ses.close()
         return dt * 1e3 / max(steps, 1), S, rows
 
+    from exact_decoding_amd import planner
     ar_ms, _, _ = time_steps(5, 0, 0, True)
     log(f"[sweep] AR step {ar_ms:.3f} ms")
+    table = []
     for N in SWEEP_N:
         for W in SWEEP_W:
             if 1 + 2 * W * (N - 1) > 2048:
                 continue
             ms, S, rows = time_steps(N, W, W, False)
+            # the pages' acceptance model (Eq. 5/7 at their fitted alpha, f)
+            # turned into a speedup on this GPU by the measured step costs
+            S_pred = planner.compression(planner.PAGES_ALPHA, N, W, planner.PAGES_F)
+            table.append({"N": N, "W": W, "step_ms": ms})
             print(json.dumps({"shape": shape.name, "N": N, "W": W, "G": W, "M": rows,
                               "step_ms": ms, "ar_step_ms": ar_ms, "break_even_S": ms / ar_ms,
-                              "measured_S": S}), flush=True)
+                              "measured_S": S, "pages_model_S": S_pred,
+                              "pages_model_speedup": S_pred * ar_ms / ms}), flush=True)
+    best = planner.best_config(table, ar_ms)
+    print(json.dumps({"shape": shape.name, "best_under_pages_model": best,
+                      "alpha": planner.PAGES_ALPHA, "f": planner.PAGES_F}), flush=True)
 
 
 def main():
