@@ -43,6 +43,18 @@ R10 Budget: the emitted tokens of the last step are truncated to max_new;
 R11 Prompt as reference: every prompt n-gram prompt[j .. j+N-1],
     j = 0 .. n-N, is inserted in increasing j before the first step.
 R12 Only lookahead harvests and the prompt feed the pool.
+R18 Sampling verification (Algorithm 4, [LD] §3.4 "Sampling verification"):
+    at position i the row predicting P+i (row 0, then the row of the
+    accepted prefix) gives weights e_v = exp((l_v - max l) / T); the
+    surviving candidates' i-th tokens are tried in candidate order, a token
+    already rejected at this position being skipped without a draw; token c
+    is accepted when r * (Z - sum of rejected weights) <= e_c for the next
+    draw r in (0, 1]; when all are rejected, the first token (index order,
+    rejected ones left out) whose running weight sum reaches u * (sum of the
+    remaining weights) is drawn and ends the step; after N-1 accepted tokens
+    one token is drawn that way from the last row.  Draw k of step s comes
+    from rng.uniform(seed, s, k), k counting the draws of the step in the
+    order they are used.  The lookahead branch stays greedy (argmax).
 """
 from __future__ import annotations
 
@@ -50,6 +62,7 @@ import dataclasses
 
 import numpy as np
 
+from . import rng
 from .model import OracleModel, argmax_lowest, causal_vis
 
 
@@ -167,6 +180,80 @@ def slide(win: np.ndarray, new: np.ndarray) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# sampling verification (R18)
+# ---------------------------------------------------------------------------
+
+def row_weights(logits_row: np.ndarray, T: float) -> np.ndarray:
+    """e_v = exp((l_v - max l) / T): softmax(l / T) up to its normaliser."""
+    l = np.asarray(logits_row, dtype=np.float64)
+    return np.exp((l - l.max()) / T)
+
+
+def draw_from(e: np.ndarray, removed: set, u: float) -> tuple[int, float]:
+    """The first token v, in index order and leaving out `removed`, whose
+    running weight sum reaches u * (sum of the remaining weights); returns
+    (v, margin), margin = distance of that threshold from the nearest running
+    sum, relative to the remaining sum."""
+    w = e.copy()
+    if removed:
+        w[list(removed)] = 0.0
+    cum = np.cumsum(w)
+    total = cum[-1]
+    target = u * total
+    v = int(np.searchsorted(cum, target, side="left"))
+    if v >= len(w):                      # rounding: the last positive weight
+        v = int(np.nonzero(w > 0)[0][-1])
+    lo = cum[v - 1] if v > 0 else 0.0
+    margin = min(target - lo, cum[v] - target) / total
+    return v, float(margin)
+
+
+def sample_verify(logits: np.ndarray, cands, N: int, base: int, T: float, seed: int,
+                  step: int):
+    """Algorithm 4 over one step's block-row logits (R18).  Returns (emit,
+    acc, g0, margin): the emitted tokens (acc accepted candidate tokens, then
+    the drawn one), the candidate whose rows are committed, and the smallest
+    decision margin of the step (relative to the normaliser in play)."""
+    k = 0
+    survivors = list(range(len(cands)))
+    row = 0
+    emit: list[int] = []
+    margin = np.inf
+    for i in range(1, N + 1):
+        e = row_weights(logits[row], T)
+        z = float(e.sum())
+        removed: set = set()
+        zr = z
+        pick = None
+        if i <= N - 1:
+            for g in survivors:
+                c = int(cands[g][i - 1])
+                if c in removed:
+                    continue
+                r = rng.uniform(seed, step, k)
+                k += 1
+                margin = min(margin, abs(r * zr - e[c]) / z)
+                if r * zr <= e[c]:
+                    pick = c
+                    break
+                removed.add(c)
+                zr -= e[c]
+        if pick is None:
+            u = rng.uniform(seed, step, k)
+            k += 1
+            t, m = draw_from(e, removed, u)
+            margin = min(margin, m)
+            emit.append(t)
+            break
+        emit.append(pick)
+        survivors = [g for g in survivors if int(cands[g][i - 1]) == pick]
+        row = base + survivors[0] * (N - 1) + (i - 1)
+    acc = len(emit) - 1
+    g0 = survivors[0] if acc > 0 else 0
+    return emit, acc, g0, margin
+
+
+# ---------------------------------------------------------------------------
 # decoding
 # ---------------------------------------------------------------------------
 
@@ -179,6 +266,7 @@ class DecodeResult:
     step_logits: list[np.ndarray]       # per step: block-row logits (if kept)
     step_rows: list[np.ndarray]         # per step: block-row tokens
     pool: NGramPool | None = None
+    margins: list[float] = dataclasses.field(default_factory=list)  # sampling: per step
 
     @property
     def S(self) -> float:
@@ -211,25 +299,34 @@ def _append(cache, new_kv, rows=None):
 
 
 def greedy_ar(model: OracleModel, prompt, max_new: int, eos_id: int = -1,
-              keep_logits: bool = False) -> DecodeResult:
-    """Plain greedy autoregressive decoding: y_{j+1} = argmax of the logits
-    at the last position given prompt and y_1..y_j ([LD] §3.4
-    "Mathematical Reformulation", the autoregressive system)."""
+              keep_logits: bool = False, temperature: float = 0.0,
+              seed: int = 0) -> DecodeResult:
+    """Plain autoregressive decoding ([LD] §3.4 "Mathematical
+    Reformulation", the autoregressive system): y_{j+1} = argmax of the
+    logits at the last position given prompt and y_1..y_j, or, with a
+    temperature, a draw from softmax(logits / T) (draw 0 of step j, R18)."""
     cache, cur = prefill(model, prompt)
     P = cache[0][0].shape[0]
     out: list[int] = []
     logits_kept = []
+    margins = []
     while len(out) < max_new:
         logits, kv = model.forward([cur], [P], causal_vis(P, 1), past=cache)
         if keep_logits:
             logits_kept.append(logits[0].copy())
         cache = _append(cache, kv)
         P += 1
-        cur = int(argmax_lowest(logits)[0])
+        if temperature > 0:
+            cur, m = draw_from(row_weights(logits[0], temperature), set(),
+                               rng.uniform(seed, len(out), 0))
+            margins.append(m)
+        else:
+            cur = int(argmax_lowest(logits)[0])
         out.append(cur)
         if eos_id >= 0 and cur == eos_id:
             break
-    return DecodeResult(out, len(out), [0] * len(out), [1] * len(out), logits_kept, [])
+    return DecodeResult(out, len(out), [0] * len(out), [1] * len(out), logits_kept, [],
+                        margins=margins)
 
 
 def score(model: OracleModel, tokens) -> np.ndarray:
@@ -243,7 +340,8 @@ def score(model: OracleModel, tokens) -> np.ndarray:
 def lookahead(model: OracleModel, prompt, N: int, W: int, G: int, max_new: int,
               init_window, prompt_ref: bool = False, pool_cap: int | None = None,
               eos_id: int = -1, keep_logits: bool = False,
-              pool: NGramPool | None = None) -> DecodeResult:
+              pool: NGramPool | None = None, temperature: float = 0.0,
+              seed: int = 0) -> DecodeResult:
     """Lookahead decoding, one step per loop iteration ([LD] §3.2, §3.4).
 
     Each step: select candidates for cur from the pool; run one forward
@@ -287,36 +385,14 @@ def lookahead(model: OracleModel, prompt, N: int, W: int, G: int, max_new: int,
             res.step_logits.append(logits)
             res.step_rows.append(toks.copy())
 
-        # greedy verification (Algorithm 3): token by token along the
-        # suffixes; survivors are the candidates that matched so far.
-        def dist_row(g, i):        # row whose output is P_i for candidate g
-            return 0 if i == 1 else base + g * (N - 1) + (i - 2)
-        survivors = list(range(len(cands)))
-        emit: list[int] = []
-        i = 1
-        while True:
-            if not survivors:
-                # fall back: accept argmax P_i (from the last surviving
-                # prefix; for i = 1 that is row 0) and stop
-                break
-            top = int(a[dist_row(survivors[0], i)])
-            matched = [g for g in survivors if cands[g][i - 1] == top]
-            if not matched:
-                break
-            emit.append(top)
-            survivors = matched
-            prev_survivors = matched
-            i += 1
-            if i > N - 1:
-                break
-        acc = len(emit)
-        if acc == 0:
-            bonus = int(a[0])
+        if temperature > 0:
+            emit, acc, g0, m = sample_verify(logits, cands, N, base, temperature, seed,
+                                             res.steps)
+            res.margins.append(m)
+            bonus = emit[-1]
+            prev_survivors = [g0]
         else:
-            # argmax P_{acc+1} from a surviving candidate
-            g0 = prev_survivors[0]
-            bonus = int(a[base + g0 * (N - 1) + (acc - 1)])
-        emit.append(bonus)
+            emit, acc, bonus, prev_survivors = _greedy_verify(a, cands, N, base)
         # commit: cur and the accepted tokens become committed rows
         committed_rows = [0]
         if acc:
@@ -345,3 +421,33 @@ def lookahead(model: OracleModel, prompt, N: int, W: int, G: int, max_new: int,
             break
     res.tokens = out
     return res
+
+
+def _greedy_verify(a, cands, N: int, base: int):
+    """Algorithm 3 on the block rows' argmax `a`, token by token along the
+    suffixes (survivors = the candidates that matched so far): returns
+    (emit, acc, bonus, survivors of the accepted prefix)."""
+    def dist_row(g, i):            # row whose output is P_i for candidate g
+        return 0 if i == 1 else base + g * (N - 1) + (i - 2)
+    survivors = list(range(len(cands)))
+    prev_survivors = [0]
+    emit: list[int] = []
+    i = 1
+    # when no candidate matches, accept argmax P_i (from the last surviving
+    # prefix; for i = 1 that is row 0) and stop
+    while survivors and i <= N - 1:
+        top = int(a[dist_row(survivors[0], i)])
+        matched = [g for g in survivors if cands[g][i - 1] == top]
+        if not matched:
+            break
+        emit.append(top)
+        survivors = prev_survivors = matched
+        i += 1
+    acc = len(emit)
+    if acc == 0:
+        bonus = int(a[0])
+    else:
+        # argmax P_{acc+1} from a surviving candidate
+        bonus = int(a[base + prev_survivors[0] * (N - 1) + (acc - 1)])
+    emit.append(bonus)
+    return emit, acc, bonus, prev_survivors

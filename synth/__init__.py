@@ -55,6 +55,10 @@ class ModelShape:
 SHAPES = {
     # fp32 tiny decoder (d 64, 4 heads, FFN 256, vocab 256, 2 layers)
     "tiny": ModelShape("tiny", 2, 64, 4, 4, 16, 256, 256, "f32"),
+    # fp32 micro decoder with an 8-token vocabulary and wide weights, so its
+    # next-token distributions are neither flat nor one-hot: sampling tests
+    # enumerate every continuation of a few tokens
+    "micro": ModelShape("micro", 1, 32, 2, 2, 16, 64, 8, "f32", init_std=0.6),
     # small bf16 decoder with the 7B head geometry (head_dim 128) used for
     # parity at sizes the oracle runs in seconds; N and vocab are chosen so the
     # GEMMs span several tiles and a ragged tail.
