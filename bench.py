@@ -48,6 +48,10 @@ def parse():
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--cpu-tokens", type=int, default=48)
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--temperature", type=float, default=0.0,
+                    help="> 0: sampling verification (Algorithm 4) at this temperature, "
+                         "for lookahead and AR alike; 0: greedy")
+    ap.add_argument("--seed", type=int, default=0, help="key of the sampling draws")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the benchmark line: step time against the row count "
                          "M over a grid of (N, W = G), one JSON line per configuration")
@@ -252,10 +256,11 @@ def main():
 
     def la_session():
         return model.session(prompt, N, W, G, args.max_new, window=window, prompt_ref=True,
-                             graph=graph)
+                             graph=graph, temperature=args.temperature, seed=args.seed)
 
     def ar_session():
-        return model.session(prompt, N, W, G, args.max_new, ar=True, graph=graph)
+        return model.session(prompt, N, W, G, args.max_new, ar=True, graph=graph,
+                             temperature=args.temperature, seed=args.seed)
 
     # warmup + steps per generation
     log("[bench] warmup")
@@ -294,7 +299,8 @@ def main():
     ses = ar_session()
     ar_tokens_ref = ses.decode()
     ses.close()
-    exact = ar_tokens_ref == la_tokens_ref
+    # (with sampling the two streams are different draws of one distribution)
+    exact = ar_tokens_ref == la_tokens_ref if args.temperature == 0 else None
 
     # per-kernel profile (HIP events around every launch, same stream)
     ses = la_session()
@@ -350,7 +356,7 @@ def main():
                                f"prompt {len(prompt)} Zipf(1.1)+3 repeated spans, prompt as reference, "
                                f"{args.max_new} new tokens per generation",
                    "N": N, "W": W, "G": G, "rows_per_step": M, "parallelism": "single GPU",
-                   "graph": graph},
+                   "graph": graph, "temperature": args.temperature},
         "step_compression": S,
         "ar_tokens_per_s": ar_tps,
         "speedup_vs_ar": la_tps / ar_tps,

@@ -26,7 +26,7 @@ EXPORTS = [
     "la_pool_stats", "la_debug_logits", "la_session_rows", "la_session_free", "la_last_error",
     "la_kernel_attention", "la_kernel_gemm", "la_kernel_gemm_ws_bytes", "la_step_profile",
     "la_kernel_attention_ws_bytes", "la_packed_bytes", "la_pack_weight", "la_probe_read",
-    "la_step_trace", "la_step_trace_bytes",
+    "la_step_trace", "la_step_trace_bytes", "la_philox_uniform",
 ]
 
 PROF_KINDS = ["gemm", "lm_head", "attention", "norm", "epilogue", "argmax", "bookkeeping"]
@@ -50,7 +50,8 @@ class DecodeParams(ctypes.Structure):
     _fields_ = [("N", ctypes.c_int32), ("W", ctypes.c_int32), ("G", ctypes.c_int32),
                 ("pool_cap", ctypes.c_int32), ("max_ctx", ctypes.c_int32),
                 ("max_new", ctypes.c_int32), ("eos_id", ctypes.c_int32),
-                ("flags", ctypes.c_uint32)]
+                ("flags", ctypes.c_uint32), ("temperature", ctypes.c_float),
+                ("reserved", ctypes.c_uint32), ("seed", ctypes.c_uint64)]
 
 
 class PoolStats(ctypes.Structure):
@@ -114,6 +115,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.la_kernel_attention_ws_bytes.restype = SZ
     lib.la_kernel_gemm.argtypes = [P, I32, I32, P, I32, P, I32, P, SZ, P]
     lib.la_probe_read.argtypes = [P, SZ, P, P]
+    lib.la_philox_uniform.argtypes = [ctypes.c_uint64, ctypes.c_uint64, I32, P, P]
     lib.la_packed_bytes.argtypes = [I32, I32]
     lib.la_packed_bytes.restype = SZ
     lib.la_pack_weight.argtypes = [P, I32, I32, P, P]
@@ -244,6 +246,12 @@ def la_kernel_attention(q, k_cache, v_cache, P, ld_ctx, k_blk, v_blk, out, H, Hk
     _check(lib.la_kernel_attention(_ptr(q), _ptr(k_cache), _ptr(v_cache), P, ld_ctx, _ptr(k_blk),
                                    _ptr(v_blk), _ptr(out), H, Hkv, hd, N, W, G, dtype, _ptr(ws),
                                    nbytes, ctypes.c_void_p(_stream_handle(stream))))
+
+
+def la_philox_uniform(seed: int, step: int, n: int, out, stream) -> None:
+    """out[i] = draw i of `step` under `seed` (device float32 tensor of >= n)."""
+    _check(load_library().la_philox_uniform(seed, step, n, _ptr(out),
+                                            ctypes.c_void_p(_stream_handle(stream))))
 
 
 def la_probe_read(buf, nbytes: int, out, stream) -> None:

@@ -15,6 +15,20 @@
 // first candidate with the longest match wins; the emitted tokens are its
 // accepted prefix plus the argmax that follows it (argmax of row 0 when
 // nothing is accepted), so every step emits 1..N tokens.
+//
+// Sampling verification ([LD] §3.4 "Sampling verification (Algorithm 4)"),
+// used when the session has a temperature T > 0: at position i the
+// distribution P_i = softmax(logits(row) / T) of the row that predicts
+// position P+i (row 0 for i = 1, then the row of the accepted prefix) is
+// tested against the surviving candidates' tokens in candidate order.  A
+// token c is accepted when a draw r in (0, 1] satisfies r <= P_i'(c), where
+// P_i' is P_i with the tokens rejected so far at this position set to zero
+// and renormalised; a rejected token is set to zero (a second candidate with
+// the same token is skipped without a draw).  When every candidate is
+// rejected, a token drawn from P_i' ends the step; after N-1 accepted tokens
+// a token drawn from P_N does.  The lookahead branch stays greedy (the window
+// and the pool use the argmax), which the pages show leaves the output
+// distribution that of sampling from the model.
 #include "la_internal.h"
 
 namespace {
@@ -112,7 +126,7 @@ __global__ __launch_bounds__(64) void k_verify(PoolDesc pool, StepIO io, RowLayo
   for (int i = lane; i < W * n1; i += 64) win[i] = io.win[i];
   __syncthreads();
 
-  if (lane == 0) {
+  if (lane == 0 && io.temp <= 0.f) {
     const int vbase = 1 + W * n1;
     const int ncand = st->ncand;
     int best = 0, bg = 0;
@@ -186,6 +200,233 @@ __global__ __launch_bounds__(64) void k_verify(PoolDesc pool, StepIO io, RowLayo
   for (int u = lane; u < W * n1; u += 64) {
     const int l = u / W, k = u - l * W;
     io.win[u] = l + 1 < n1 ? win[(l + 1) * W + k] : a[1 + (n1 - 1) * W + k];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Counter-based draws: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel
+// Random Numbers: As Easy as 1, 2, 3", SC 2011): per round two 32x32-bit
+// products with the multipliers 0xD2511F53 and 0xCD9E8D57, the key advanced
+// by 0x9E3779B9 / 0xBB67AE85 between rounds, ten rounds.  Draw k of step s
+// under seed x is word 0 of Philox((s lo, s hi, k, 0), (x lo, x hi)), mapped
+// to ((w >> 8) + 1) * 2^-24 in (0, 1].
+__device__ __forceinline__ uint32_t philox_w0(unsigned long long seed, unsigned long long step,
+                                              uint32_t k) {
+  uint32_t c0 = (uint32_t)step, c1 = (uint32_t)(step >> 32), c2 = k, c3 = 0;
+  uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+#pragma unroll
+  for (int rnd = 0; rnd < 10; ++rnd) {
+    if (rnd) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
+    const uint32_t lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
+    const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
+  }
+  return c0;
+}
+__device__ __forceinline__ float draw01(unsigned long long seed, unsigned long long step,
+                                        uint32_t k) {
+  return (float)((philox_w0(seed, step, k) >> 8) + 1u) * (1.0f / 16777216.0f);
+}
+
+__global__ void k_philox_uniform(unsigned long long seed, unsigned long long step, int n,
+                                 float* out) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = draw01(seed, step, (uint32_t)i);
+}
+
+constexpr int SV_T = 1024;  // threads of the sampling verification
+
+// One workgroup.  e[v] = exp((logit_v - max) / T) of the current row lives in
+// LDS; thread t owns the contiguous vocabulary slice [t*CH, (t+1)*CH).
+// Sums: each thread adds its slice in index order; the 1024 slice sums are
+// added by a fixed halving tree (Z) or scanned (wave scans by shuffles, then
+// the 16 wave totals in order) for the residual draw.
+__global__ __launch_bounds__(SV_T) void k_sample_verify(StepIO io, RowLayout L) {
+  __shared__ float e[SAMPLE_VMAX];
+  __shared__ float red[SV_T];
+  __shared__ float wtot[SV_T / 64];
+  __shared__ int32_t removed[VMAX_M];
+  __shared__ int32_t surv[VMAX_M];
+  __shared__ int s_nrem, s_pick, s_nsurv, s_row, s_done_pos;
+  __shared__ float s_target;
+  __shared__ int32_t emitted[LA_MAX_N];  // accepted tokens, then the drawn one
+  DevState* st = io.st;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int n1 = L.N - 1, V = io.V;
+  const int vbase = 1 + L.W * n1;
+  const int CH = (V + SV_T - 1) / SV_T;
+  const int v0 = min(V, tid * CH), v1 = min(V, v0 + CH);
+  const unsigned long long step = (unsigned long long)st->stats[ST_STEPS];
+  const int ncand = st->ncand;
+  uint32_t k = 0;  // draws used (same on every thread)
+
+  // load row `row`'s weights into e[], return Z (fixed order)
+  auto weights = [&](int row) -> float {
+    const float* lg = io.logits + (size_t)row * V;
+    float m = -INFINITY;
+    for (int v = v0; v < v1; ++v) m = fmaxf(m, lg[v]);
+    red[tid] = m;
+    __syncthreads();
+    for (int s = SV_T / 2; s > 0; s >>= 1) {
+      if (tid < s) red[tid] = fmaxf(red[tid], red[tid + s]);
+      __syncthreads();
+    }
+    const float mx = red[0];
+    __syncthreads();
+    float sum = 0.f;
+    for (int v = v0; v < v1; ++v) {
+      const float w = expf((lg[v] - mx) / io.temp);
+      e[v] = w;
+      sum += w;
+    }
+    red[tid] = sum;
+    __syncthreads();
+    for (int s = SV_T / 2; s > 0; s >>= 1) {
+      if (tid < s) red[tid] += red[tid + s];
+      __syncthreads();
+    }
+    const float z = red[0];
+    __syncthreads();
+    return z;
+  };
+  // residual draw: the first token v (index order, not removed) whose
+  // running sum of weights reaches u * (sum of the remaining weights)
+  auto residual = [&](float u) -> int {
+    const int nrem = s_nrem;
+    float sum = 0.f;
+    for (int v = v0; v < v1; ++v) {
+      bool rm = false;
+      for (int j = 0; j < nrem; ++j) rm = rm || removed[j] == v;
+      if (!rm) sum += e[v];
+    }
+    // inclusive scan of the slice sums within the wave, then the wave
+    // totals in order; a slice covers (excl, incl], and the next slice's
+    // excl is this slice's incl, so exactly one slice holds the target
+    float x = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    const float xprev = __shfl_up(x, 1, 64);
+    if (lane == 63) wtot[wv] = x;
+    if (tid == 0) s_pick = -1;
+    __syncthreads();
+    float before = 0.f;
+    for (int w = 0; w < wv; ++w) before += wtot[w];
+    float total = 0.f;
+    for (int w = 0; w < SV_T / 64; ++w) total += wtot[w];
+    const float incl = before + x;
+    const float excl = lane == 0 ? before : before + xprev;
+    const float target = u * total;
+    if (sum > 0.f && excl < target && incl >= target) {
+      float run = excl;
+      int pick = -1;
+      for (int v = v0; v < v1; ++v) {
+        bool rm = false;
+        for (int j = 0; j < nrem; ++j) rm = rm || removed[j] == v;
+        if (rm) continue;
+        run += e[v];
+        if (run >= target) { pick = v; break; }
+      }
+      if (pick < 0) {  // rounding inside the slice: its last positive weight
+        for (int v = v1 - 1; v >= v0; --v) {
+          bool rm = false;
+          for (int j = 0; j < nrem; ++j) rm = rm || removed[j] == v;
+          if (!rm && e[v] > 0.f) { pick = v; break; }
+        }
+      }
+      s_pick = pick;
+    }
+    __syncthreads();
+    if (s_pick < 0 && tid == 0) {
+      // target beyond the scanned total by rounding: the last positive weight
+      for (int v = V - 1; v >= 0; --v) {
+        bool rm = false;
+        for (int j = 0; j < nrem; ++j) rm = rm || removed[j] == v;
+        if (!rm && e[v] > 0.f) { s_pick = v; break; }
+      }
+    }
+    __syncthreads();
+    return s_pick;
+  };
+
+  if (tid == 0) {
+    s_nsurv = ncand;
+    s_row = 0;
+  }
+  for (int g = tid; g < ncand; g += SV_T) surv[g] = g;
+  __syncthreads();
+  int acc = 0, last = -1;
+  for (int i = 1; i <= n1 + 1; ++i) {
+    const float z = weights(s_row);
+    if (tid == 0) {
+      s_nrem = 0;
+      s_pick = -1;
+      s_done_pos = 1;
+      float zr = z;
+      if (i <= n1) {
+        for (int j = 0; j < s_nsurv; ++j) {
+          const int c = io.cand[surv[j] * n1 + i - 1];
+          bool seen = false;
+          for (int q = 0; q < s_nrem; ++q) seen = seen || removed[q] == c;
+          if (seen) continue;
+          const float r = draw01(io.seed, step, k++);
+          if (r * zr <= e[c]) { s_pick = c; break; }
+          removed[s_nrem++] = c;
+          zr -= e[c];
+        }
+      }
+      if (s_pick >= 0) {
+        // survivors: candidates whose i-th token is the accepted one
+        int ns = 0;
+        for (int j = 0; j < s_nsurv; ++j)
+          if (io.cand[surv[j] * n1 + i - 1] == s_pick) surv[ns++] = surv[j];
+        s_nsurv = ns;
+        s_row = vbase + surv[0] * n1 + (i - 1);
+        s_done_pos = 0;
+      } else {
+        s_target = draw01(io.seed, step, k++);
+      }
+    }
+    __syncthreads();
+    if (!s_done_pos) {
+      if (tid == 0) emitted[acc] = s_pick;
+      ++acc;
+      __syncthreads();
+      continue;
+    }
+    const int t = residual(s_target);
+    last = t;
+    break;
+  }
+  if (tid == 0) {
+    // commit: row 0 and the accepted candidate rows become cache rows
+    st->commit_p = st->P;
+    st->commit_n = acc + 1;
+    st->commit_rows[0] = 0;
+    const int g0 = acc > 0 ? surv[0] : 0;
+    for (int j = 1; j <= acc; ++j) st->commit_rows[j] = vbase + g0 * n1 + j - 1;
+    st->P += acc + 1;
+    emitted[acc] = last;
+    const int room = io.max_new - st->total;
+    int n = 0, done = 0;
+    for (int j = 0; j <= acc && n < room; ++j) {
+      st->out[n++] = emitted[j];
+      if (io.eos >= 0 && emitted[j] == io.eos) { done = 1; break; }
+    }
+    st->n_out = n;
+    st->total += n;
+    if (st->total >= io.max_new) done = 1;
+    if (done) st->done = 1;
+    st->cur = last;
+    st->stats[ST_HIST0 + acc] += 1;
+    st->stats[ST_STEPS] += 1;
+    st->stats[ST_TOKENS] += n;
   }
 }
 
@@ -267,6 +508,21 @@ hipError_t launch_verify(const PoolDesc& pool, const StepIO& io, const RowLayout
                          hipStream_t st) {
   if (lay.M > VMAX_M) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_verify, dim3(1), dim3(64), 0, st, pool, io, lay);
+  return hipGetLastError();
+}
+
+hipError_t launch_sample_verify(const StepIO& io, const RowLayout& lay, hipStream_t st) {
+  if (lay.M > VMAX_M || io.V > SAMPLE_VMAX || io.V < 1 || !(io.temp > 0.f))
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_sample_verify, dim3(1), dim3(SV_T), 0, st, io, lay);
+  return hipGetLastError();
+}
+
+hipError_t launch_philox_uniform(unsigned long long seed, unsigned long long step, int n,
+                                 float* out, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_philox_uniform, dim3((n + 255) / 256), dim3(256), 0, st, seed, step, n,
+                     out);
   return hipGetLastError();
 }
 

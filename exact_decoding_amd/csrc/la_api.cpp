@@ -179,6 +179,11 @@ int check_params(const la_model* m, const la_decode_params* p) {
   const long long W = ar ? 0 : p->W, G = ar ? 0 : p->G;
   const long long M = 1 + (W + G) * (p->N - 1);
   if (M > 2048) return fail(LA_EINVAL, "1 + (W+G)(N-1) must be <= 2048");
+  if (p->reserved != 0) return fail(LA_EINVAL, "reserved must be 0");
+  if (!(p->temperature >= 0.f) || !std::isfinite(p->temperature))
+    return fail(LA_EINVAL, "temperature must be finite and >= 0");
+  if (p->temperature > 0.f && m->d.vocab > SAMPLE_VMAX)
+    return fail(LA_EINVAL, "sampling needs vocab <= 32768");
   return LA_OK;
 }
 
@@ -410,6 +415,10 @@ int enqueue_step(la_session* ss) {
   io.amax = ss->at<int32_t>(ss->v.amax);
   io.max_new = ss->p.max_new;
   io.eos = ss->p.eos_id;
+  io.logits = ss->at<float>(ss->v.logits);
+  io.V = s.V;
+  io.temp = ss->p.temperature;
+  io.seed = (unsigned long long)ss->p.seed;
 
   const double R = s.M, ES = (double)dtype_size(dt);
   LA_KP(LA_PROF_BOOK, 0, 0, launch_gather(pool, io, ss->lay, st), "gather");
@@ -443,6 +452,8 @@ int enqueue_step(la_session* ss) {
   LA_KP(LA_PROF_ARGMAX, R * s.V * 4.0, 0,
         launch_argmax(ss->at<float>(ss->v.logits), s.M, s.V, ss->at<int32_t>(ss->v.amax), st),
         "argmax");
+  if (io.temp > 0.f)
+    LA_KP(LA_PROF_BOOK, 0, 0, launch_sample_verify(io, ss->lay, st), "sample_verify");
   LA_KP(LA_PROF_BOOK, 0, 0, launch_verify(pool, io, ss->lay, st), "verify");
   KvCommit c{};
   c.st = io.st;
@@ -482,6 +493,9 @@ int la_model_load(const la_model_desc* d, const void* const* dev_weights, int n_
   const int hd = d->head_dim;
   if (hd != 16 && hd != 32 && hd != 64 && hd != 128) return fail(LA_EINVAL, "head_dim must be 16, 32, 64 or 128");
   if (!(d->norm_eps > 0.f) || !(d->rope_theta > 0.f)) return fail(LA_EINVAL, "norm_eps and rope_theta must be > 0");
+  // the residual + RMSNorm epilogue gives each row whole waves of columns
+  if (d->d_model % 64 || d->d_model > 16384)
+    return fail(LA_EINVAL, "d_model must be a multiple of 64, at most 16384");
   if (d->dtype == LA_BF16) {
     const int hq = d->n_heads * hd, hk = d->n_kv_heads * hd;
     if (d->d_model % 64 || hq % 128 || hk % 128 || d->d_ff % 128)
@@ -806,6 +820,12 @@ int la_kernel_attention(const void* q, const void* k_cache, const void* v_cache,
     a.tail_ml = a.tail_o + (size_t)M * H * hd;
   }
   LA_HIP(launch_attention(a, dtype, (hipStream_t)hip_stream));
+  return LA_OK;
+}
+
+int la_philox_uniform(uint64_t seed, uint64_t step, int32_t n, float* out, void* hip_stream) {
+  if (n < 0 || (n > 0 && !out)) return fail(LA_EINVAL, "bad argument");
+  LA_HIP(launch_philox_uniform(seed, step, n, out, (hipStream_t)hip_stream));
   return LA_OK;
 }
 

@@ -201,11 +201,22 @@ struct StepIO {
   int32_t* pos;   // [M]
   const int32_t* amax;  // [M]
   int max_new, eos;
+  // sampling verification ([LD] §3.4 "Sampling verification (Algorithm 4)");
+  // temp == 0: greedy verification
+  const float* logits;  // [M][V]
+  int V;
+  float temp;
+  unsigned long long seed;
 };
 hipError_t launch_gather(const PoolDesc& pool, const StepIO& io, const RowLayout& lay,
                          hipStream_t st);
 hipError_t launch_verify(const PoolDesc& pool, const StepIO& io, const RowLayout& lay,
                          hipStream_t st);
+// Largest vocabulary the sampling verification keeps in LDS.
+constexpr int SAMPLE_VMAX = 32768;
+hipError_t launch_sample_verify(const StepIO& io, const RowLayout& lay, hipStream_t st);
+hipError_t launch_philox_uniform(unsigned long long seed, unsigned long long step, int n,
+                                 float* out, hipStream_t st);
 struct KvCommit {
   const DevState* st;
   const void* kb; const void* vb;  // [L][M][Hkv*hd]

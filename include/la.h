@@ -70,10 +70,20 @@ typedef struct {
  *            LA_AR: plain greedy autoregressive decoding through the same
  *              kernels (W = G = 0 internally; one token per step).
  *            LA_NO_GRAPH: launch every step's kernels eagerly instead of
- *              replaying a captured HIP graph. */
+ *              replaying a captured HIP graph.
+ * temperature  0: greedy verification ([LD] §3.4 "Greedy verification
+ *              algorithm (Algorithm 3)").  > 0: sampling verification
+ *              ([LD] §3.4 "Sampling verification (Algorithm 4)") against
+ *              softmax(logits / temperature); the lookahead branch stays
+ *              greedy.  Needs vocab <= 32768.  With LA_AR: plain sampling.
+ * seed       key of the step's draws (Philox4x32-10, counter = (step, draw
+ *              index); see la_philox_uniform). */
 typedef struct {
   int32_t N, W, G, pool_cap, max_ctx, max_new, eos_id;
   uint32_t flags;
+  float temperature;
+  uint32_t reserved;  /* must be 0 */
+  uint64_t seed;
 } la_decode_params;
 
 #define LA_PROMPT_REF 1u
@@ -113,9 +123,11 @@ int la_pack_weight(const void* src, int32_t N, int32_t K, void* dst, void* hip_s
  *   lm_head [vocab][d].
  * fp32 models: matrices row-major [out][in].  bf16 models: wq, wk, wv, wo,
  * wg, wu, wd and lm_head in the packed layout above (la_pack_weight); emb
- * and the norm gains row-major.  They must stay valid until la_model_free.  bf16 models need d, H*hd and d_ff to be
- * multiples of 64 and H*hd, Hkv*hd multiples of 128; head_dim <= 128 and
- * even.  *out receives a library-owned handle. */
+ * and the norm gains row-major.  They must stay valid until la_model_free.
+ * Every model needs d a multiple of 64 (at most 16384), head_dim 16, 32, 64
+ * or 128, and H a multiple of Hkv; bf16 models also need H*hd, Hkv*hd and
+ * d_ff multiples of 128.  LA_EINVAL otherwise.  *out receives a
+ * library-owned handle. */
 int la_model_load(const la_model_desc* d, const void* const* dev_weights, int n_weights,
                   void* hip_stream, la_model** out);
 void la_model_free(la_model* m);
@@ -142,8 +154,9 @@ int la_prefill(la_model* m, const la_decode_params* p, const int32_t* prompt, in
 
 /* One lookahead decoding step: candidate gather, one forward pass over
  * M = 1 + (W+G)(N-1) rows under the lookahead mask ([LD] §3.4 "The custom
- * attention mask (Figure 2)"), greedy verification (Algorithm 3), KV
- * commit, window slide and pool insert.  Blocks until the emitted tokens
+ * attention mask (Figure 2)"), greedy verification (Algorithm 3) or, with a
+ * temperature, sampling verification (Algorithm 4), KV commit, window slide
+ * and pool insert.  Blocks until the emitted tokens
  * are on the host.
  * out_tokens: host pointer with room for out_cap >= N ids.
  * *n_out: tokens written (1..N while decoding; fewer on the last step).
@@ -239,6 +252,14 @@ size_t la_kernel_attention_ws_bytes(int32_t ld_ctx, int32_t H, int32_t hd, int32
 int la_kernel_gemm(const void* x, int32_t M, int32_t K, const void* w, int32_t N, float* y,
                    int32_t dtype, void* ws, size_t ws_bytes, void* hip_stream);
 size_t la_kernel_gemm_ws_bytes(int32_t M, int32_t K, int32_t N);
+
+/* The draws of sampling verification (test hook): out[i] = draw i of step
+ * `step` under `seed`, i < n: word 0 of Philox4x32-10 (Salmon et al., "Parallel
+ * Random Numbers: As Easy as 1, 2, 3", SC 2011) at counter (step mod 2^32,
+ * step >> 32, i, 0) and key (seed mod 2^32, seed >> 32), mapped to
+ * ((word >> 8) + 1) / 2^24 in (0, 1].  out: device, n floats.  Enqueued on
+ * `hip_stream`. */
+int la_philox_uniform(uint64_t seed, uint64_t step, int32_t n, float* out, void* hip_stream);
 
 /* HBM read probe (benchmark hook): reads `bytes` (a multiple of 16) from the
  * device buffer `buf` with 16-byte loads across the whole chip and writes one

@@ -28,6 +28,8 @@ from oracle import rng
 from oracle import lookahead as LA
 from oracle.model import OracleModel
 
+from sampling_util import MICRO_PROMPT, _gof, _softmax, exact_ar_probs
+
 HERE = os.path.dirname(__file__)
 
 
@@ -48,30 +50,6 @@ def test_draws_uniform_on_open_closed_interval():
     assert stats.chisquare(counts).pvalue > 1e-3
     # different keys and counters give different streams
     assert rng.uniform(1, 0, 0) != rng.uniform(2, 0, 0) != rng.uniform(1, 1, 0)
-
-
-def _softmax(l, T):
-    p = np.exp((l - l.max()) / T)
-    return p / p.sum()
-
-
-def _gof(counts: dict, probs: dict, n: int, min_expected: float = 5.0) -> float:
-    """Chi-square p-value of observed counts against probabilities, rare
-    cells pooled."""
-    obs, exp, rare_o, rare_e = [], [], 0, 0.0
-    for key, p in probs.items():
-        if p * n < min_expected:
-            rare_o += counts.get(key, 0)
-            rare_e += p * n
-        else:
-            obs.append(counts.get(key, 0))
-            exp.append(p * n)
-    if rare_e > 0:
-        obs.append(rare_o)
-        exp.append(rare_e)
-    obs, exp = np.array(obs, float), np.array(exp, float)
-    exp *= obs.sum() / exp.sum()
-    return stats.chisquare(obs, exp).pvalue
 
 
 def test_one_step_is_rejection_sampling():
@@ -131,27 +109,6 @@ def micro():
     s = synth.SHAPES["micro"]
     w = [synth.gen_tensor(s, 0, i) for i in range(len(synth.weight_names(s)))]
     return OracleModel(s, w)
-
-
-def exact_ar_probs(model, prompt, k: int, T: float) -> dict:
-    """P(y_1..y_k) = product of softmax(logits / T) conditionals, every
-    continuation of the 8-token vocabulary enumerated."""
-    V = model.s.vocab
-    out = {}
-    for seq in itertools.product(range(V), repeat=k - 1):
-        lg = LA.score(model, list(prompt) + list(seq))
-        p = 1.0
-        for j, t in enumerate(seq):
-            p *= _softmax(lg[len(prompt) - 1 + j], T)[t]
-        last = _softmax(lg[len(prompt) - 1 + k - 1], T)
-        for t in range(V):
-            out[tuple(seq) + (t,)] = p * last[t]
-    return out
-
-
-# the start of the model's own greedy continuation of [0], so the prompt's n-grams
-# are likely continuations and candidates are accepted in most first steps
-MICRO_PROMPT = [0, 2, 2, 2, 2, 2, 2, 7, 4, 7, 4, 7, 4]
 
 
 def test_ar_sampling_matches_enumeration(micro):
