@@ -45,7 +45,11 @@ def test_model_load_validation():
     assert _model(hd=96)[0] == B.LA_EINVAL
     assert _model(H=4, Hkv=3)[0] == B.LA_EINVAL
     assert _model(d=500)[0] == B.LA_EINVAL          # bf16 needs d % 64 == 0
-    assert _model(dtype=B.LA_F32, d=500, H=4, hd=16, F=100)[0] == B.LA_OK
+    # every model: d a multiple of 64 (the norm epilogue's whole waves per row)
+    assert _model(dtype=B.LA_F32, d=500, H=4, hd=16, F=100)[0] == B.LA_EINVAL
+    rc, m = _model(dtype=B.LA_F32, d=64, H=4, hd=16, F=100)
+    assert rc == B.LA_OK
+    B.la_model_free(m)
     assert _model(dtype=7)[0] == B.LA_EINVAL
 
 
@@ -56,10 +60,18 @@ def test_session_bytes_and_param_validation():
     assert n > 0
     p_ar = B.DecodeParams(5, 15, 15, 0, 400, 256, -1, B.LA_AR)
     assert 0 < B.la_session_bytes(m, p_ar) < n
+    # a temperature and a seed change nothing in the workspace
+    p_s = B.DecodeParams(5, 15, 15, 0, 400, 256, -1, B.LA_PROMPT_REF, 0.8, 0, 12345)
+    assert B.la_session_bytes(m, p_s) == n
     for bad in [B.DecodeParams(1, 4, 4, 0, 100, 10, -1, 0), B.DecodeParams(17, 4, 4, 0, 100, 10, -1, 0),
                 B.DecodeParams(3, -1, 4, 0, 100, 10, -1, 0), B.DecodeParams(3, 4, 4, 0, 100, 0, -1, 0),
                 B.DecodeParams(3, 4, 4, 0, 100, 10, 4000, 0), B.DecodeParams(3, 4, 4, 0, 100, 10, -1, 64),
-                B.DecodeParams(16, 100, 100, 0, 100, 10, -1, 0)]:
+                B.DecodeParams(16, 100, 100, 0, 100, 10, -1, 0),
+                # sampling: negative or non-finite temperature, reserved field set
+                B.DecodeParams(3, 4, 4, 0, 100, 10, -1, 0, -0.5, 0, 1),
+                B.DecodeParams(3, 4, 4, 0, 100, 10, -1, 0, float("nan"), 0, 1),
+                B.DecodeParams(3, 4, 4, 0, 100, 10, -1, 0, float("inf"), 0, 1),
+                B.DecodeParams(3, 4, 4, 0, 100, 10, -1, 0, 1.0, 7, 1)]:
         with pytest.raises(B.LaError) as e:
             B.la_session_bytes(m, bad)
         assert e.value.code == B.LA_EINVAL
