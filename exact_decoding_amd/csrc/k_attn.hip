@@ -128,17 +128,36 @@ __device__ __forceinline__ float dot_half(const float* qs, const u32x4_t (&k)[HD
   return (a[0] + a[1]) + (a[2] + a[3]);
 }
 
+// LDS ordering inside one wave: its LDS writes are complete and visible to
+// all of its lanes (the per-row part uses wave-private LDS).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 template <typename T, int HD>
-__global__ __launch_bounds__(64) void k_attn_tail(AttnDesc a) {
+struct TailLds {
+  static constexpr int VSTRIDE = HD + 16 / (int)sizeof(T);  // padded LDS row of V
+  float qs[HD];
+  float ps[TT];
+  T vs[TT * VSTRIDE] __attribute__((aligned(16)));
+};
+
+// The per-row part of row r, head h, by one wave (all 64 lanes) on its own
+// TailLds; writes the row's normalised output.
+template <typename T, int HD>
+__device__ __forceinline__ void tail_row(const AttnDesc& a, int h, int r, TailLds<T, HD>& L) {
   constexpr int NV = HD * (int)sizeof(T) / 16;       // 16-byte words per K / V row
   constexpr int NH = NV / 2;                         // words per half row (one lane)
   constexpr int DPL = HD >= 64 ? HD / 64 : 1;        // output dims per lane (contiguous)
-  constexpr int VSTRIDE = HD + 16 / (int)sizeof(T);  // padded LDS row of V
+  constexpr int VSTRIDE = TailLds<T, HD>::VSTRIDE;
   static_assert(NV % 2 == 0, "a lane holds half a row");
-  __shared__ float qs[HD];
-  __shared__ float ps[TT];
-  __shared__ __align__(16) T vs[TT * VSTRIDE];
-  const int h = blockIdx.x, r = blockIdx.y, lane = threadIdx.x;
+  float* qs = L.qs;
+  float* ps = L.ps;
+  T* vs = L.vs;
+  const int lane = threadIdx.x & 63;
   const int slot = lane >> 1, half = lane & 1;
   const int kvh = h * a.Hkv / a.H;
   const int Pc = a.Pdev ? *a.Pdev : a.P_host;
@@ -198,7 +217,7 @@ __global__ __launch_bounds__(64) void k_attn_tail(AttnDesc a) {
       for (int e = 0; e < NH; ++e)
         *(u32x4_t*)((char*)(vs + slot * VSTRIDE + half * (HD / 2)) + 16 * e) = vr[e];
     }
-    __syncthreads();
+    wave_lds_sync();
     const float mine = on ? dot_half<HD>(qs + half * (HD / 2), kr, T()) : 0.f;
     const float other = __shfl_xor(mine, 1, 64);
     const float sc = on ? ((half ? other : mine) + (half ? mine : other)) * scale : -INFINITY;
@@ -206,7 +225,7 @@ __global__ __launch_bounds__(64) void k_attn_tail(AttnDesc a) {
     const float pv = on ? expf(sc - mp) : 0.f;
     if (!half) ps[slot] = pv;
     const float lp = wave_sum(half ? 0.f : pv);
-    __syncthreads();
+    wave_lds_sync();
     // P.V over this tile: key j goes to partial j mod 4
     float acc[4][DPL];
 #pragma unroll
@@ -235,7 +254,7 @@ __global__ __launch_bounds__(64) void k_attn_tail(AttnDesc a) {
     for (int j = 0; j < DPL; ++j)
       o[j] = o[j] * ca + ((acc[0][j] + acc[1][j]) + (acc[2][j] + acc[3][j])) * cb;
     m_run = mn;
-    __syncthreads();
+    wave_lds_sync();
   }
 
   // merge: the MFMA chunks of [0, F) in chunk order, then this row's part
@@ -276,6 +295,12 @@ __global__ __launch_bounds__(64) void k_attn_tail(AttnDesc a) {
     for (int j = 0; j < DPL; ++j) st_f(out + d0 + j, oo[j] * inv);
 }
 
+template <typename T, int HD>
+__global__ __launch_bounds__(64) void k_attn_tail(AttnDesc a) {
+  __shared__ TailLds<T, HD> L;
+  tail_row<T, HD>(a, blockIdx.x, blockIdx.y, L);
+}
+
 // MFMA part (bf16, head_dim 128): one workgroup per (head, prefix chunk
 // committed positions, block of 128 rows).  Each 64-position tile of K and V
 // is staged in LDS once and used by every row; wave w handles the 16-row
@@ -293,6 +318,123 @@ __global__ __launch_bounds__(64) void k_attn_tail(AttnDesc a) {
 constexpr int KSTR = 128 + 8;  // LDS row stride of K (bf16)
 constexpr int VSTR = AT + 8;   // LDS row stride of V^T (bf16)
 
+// One 16-row group: its rows' bulk ends F (lane's row = c16) and Q^T
+// fragments (zero for rows past `nrows`).
+__device__ __forceinline__ void group_load(const AttnDesc& a, int h, int Pc, int row0, int nrows,
+                                           int c16, int q4, int& F, U4 (&qf)[4]) {
+  const int r = row0 + c16;
+  F = 0;
+  if (c16 < nrows) {
+    const int pos = row_pos(a, r, Pc);
+    const int P = a.causal_cache ? pos + 1 : Pc;
+    F = bulk_end(pos, P, a.D);
+  }
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    if (c16 < nrows)
+      qf[ks].u = *(const u32x4_t*)((const bf16_t*)a.q + (size_t)r * a.H * 128 + h * 128 +
+                                   ks * 32 + q4 * 8);
+    else
+      qf[ks].u = u32x4_t{0u, 0u, 0u, 0u};
+  }
+}
+
+// One group's online-softmax update from the 64-key tile [t0, t0 + 64)
+// staged in Ks / Vt; keys at or past a row's F are masked.
+__device__ __forceinline__ void group_tile(const bf16_t* Ks, const bf16_t* Vt, int t0, int F,
+                                           const U4 (&qf)[4], f32x4_t (&o)[8], float& m_run,
+                                           float& l_run, int c16, int q4, float scale) {
+  // keys [t0, F) of the tile are this lane's row's (F a multiple of BT)
+  const int nv = F - t0;
+  // skip the group when the tile is past every one of its rows
+  if (!__any(nv > 0)) return;
+  f32x4_t st[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    st[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      U4 ka;
+      ka.u = *(const u32x4_t*)(&Ks[(kb * 16 + c16) * KSTR + ks * 32 + q4 * 8]);
+      st[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka.v, qf[ks].v, st[kb], 0, 0, 0);
+    }
+  }
+  float mt = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float sv = kb * 16 + 4 * q4 + e < nv ? st[kb][e] * scale : -INFINITY;
+      st[kb][e] = sv;
+      mt = fmaxf(mt, sv);
+    }
+  mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+  mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+  const float m_new = fmaxf(m_run, mt);
+  const float alpha = m_new == -INFINITY ? 1.0f : expf(m_run - m_new);
+  // p enters the PV product as the sum of two bf16 values, hi = bf16(p)
+  // and lo = bf16(p - hi) (p - hi is exact in fp32), so the product
+  // carries p to about 2^-17 relative, as an fp32 product would: no
+  // rounding of the probabilities beyond the fp32 arithmetic
+  float ls = 0.f;
+  U4 pa[2], pl[2];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float pv = kb * 16 + 4 * q4 + e < nv ? expf(st[kb][e] - m_new) : 0.f;
+      ls += pv;
+      const uint16_t hb = f2bf(pv);
+      pa[kb >> 1].h[(kb & 1) * 4 + e] = hb;
+      pl[kb >> 1].h[(kb & 1) * 4 + e] = f2bf(pv - __uint_as_float((uint32_t)hb << 16));
+    }
+  ls += __shfl_xor(ls, 16, 64);
+  ls += __shfl_xor(ls, 32, 64);
+  l_run = l_run * alpha + ls;
+  m_run = m_new;
+  // rescale O rows 4*q4 + e by their row's alpha (held by lane 4*q4 + e)
+  float al[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) al[e] = __shfl(alpha, q4 * 4 + e, 64);
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[db][e] *= al[e];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const bf16_t* vr = &Vt[(db * 16 + c16) * VSTR + 32 * j + 4 * q4];
+      U4 vb;
+      const u32x2_t lo = *(const u32x2_t*)vr;
+      const u32x2_t hi = *(const u32x2_t*)(vr + 16);
+      vb.u = u32x4_t{lo.x, lo.y, hi.x, hi.y};
+      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[j].v, vb.v, o[db], 0, 0, 0);
+      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl[j].v, vb.v, o[db], 0, 0, 0);
+    }
+  }
+}
+
+// A group's (m, l) and unnormalised O of one chunk -> part_ml / part_o.
+__device__ __forceinline__ void group_store(const AttnDesc& a, int split, int h, int row0,
+                                            int nrows, const f32x4_t (&o)[8], float m_run,
+                                            float l_run, int lane) {
+  const int c16 = lane & 15, q4 = lane >> 4;
+  if (lane < 16 && c16 < nrows) {
+    float* pm = a.part_ml + (((size_t)split * a.rows + row0 + c16) * a.H + h) * 2;
+    pm[0] = m_run;
+    pm[1] = l_run;
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int rl = q4 * 4 + e;
+    if (rl >= nrows) continue;
+    float* po = a.part_o + (((size_t)split * a.rows + row0 + rl) * a.H + h) * 128;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) po[db * 16 + c16] = o[db][e];
+  }
+}
+
 __global__ __launch_bounds__(256) void k_attn_bulk(AttnDesc a) {
   __shared__ __align__(16) bf16_t Ks[AT * KSTR];
   __shared__ __align__(16) bf16_t Vt[128 * VSTR];
@@ -309,33 +451,18 @@ __global__ __launch_bounds__(256) void k_attn_bulk(AttnDesc a) {
   const bf16_t* vc = (const bf16_t*)a.vc + (size_t)kvh * a.ld_ctx * 128;
   const float scale = 1.0f / sqrtf(128.0f);
 
-  // this wave's row groups; per lane: row = group*16 + c16
+  // this wave's row groups w and w + 4
   int F[2];
   bool gon[2];
   U4 qf[2][4];
   f32x4_t o[2][8];
   float m_run[2], l_run[2];
-  int tend = 0;  // tiles below this may be valid for some row of the workgroup
 #pragma unroll
   for (int gi = 0; gi < 2; ++gi) {
     const int g = wave + 4 * gi;
     gon[gi] = g < ngroups;
-    const int rl = g * 16 + c16;
-    const int r = row0 + rl;
-    F[gi] = 0;
-    if (gon[gi] && rl < nrows) {
-      const int pos = row_pos(a, r, Pc);
-      const int P = a.causal_cache ? pos + 1 : Pc;
-      F[gi] = bulk_end(pos, P, a.D);
-    }
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      if (gon[gi] && rl < nrows)
-        qf[gi][ks].u = *(const u32x4_t*)((const bf16_t*)a.q + (size_t)r * a.H * 128 + h * 128 +
-                                       ks * 32 + q4 * 8);
-      else
-        qf[gi][ks].u = u32x4_t{0u, 0u, 0u, 0u};
-    }
+    group_load(a, h, Pc, row0 + g * 16, gon[gi] ? min(16, nrows - g * 16) : 0, c16, q4, F[gi],
+               qf[gi]);
 #pragma unroll
     for (int db = 0; db < 8; ++db) o[gi][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     m_run[gi] = -INFINITY;
@@ -347,7 +474,7 @@ __global__ __launch_bounds__(256) void k_attn_bulk(AttnDesc a) {
   __syncthreads();
   atomicMax(&s_fmax, max(F[0], F[1]));
   __syncthreads();
-  tend = min(attn_chunk_start(split + 1), s_fmax);
+  const int tend = min(attn_chunk_start(split + 1), s_fmax);
   // no row of the workgroup has keys in this chunk: the per-row kernel reads
   // none of its partials
   if (tend <= s0) return;
@@ -381,7 +508,7 @@ __global__ __launch_bounds__(256) void k_attn_bulk(AttnDesc a) {
     vb0.u = v0k + 1 < tend ? b0 : z4;
     vb1.u = v0k + 1 < tend ? b1 : z4;
   };
-  if (s0 < tend) fetch(s0);
+  fetch(s0);
   for (int t0 = s0; t0 < tend; t0 += AT) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) *(u32x4_t*)(&Ks[fkey * KSTR + fseg * 32 + j * 8]) = kf[j];
@@ -395,103 +522,15 @@ __global__ __launch_bounds__(256) void k_attn_bulk(AttnDesc a) {
     __syncthreads();
     if (t0 + AT < tend) fetch(t0 + AT);
 #pragma unroll
-    for (int gi = 0; gi < 2; ++gi) {
-      if (!gon[gi]) continue;
-      // keys [t0, F) of the tile are this lane's row's (F a multiple of BT)
-      const int nv = F[gi] - t0;
-      // skip the group when the tile is past every one of its rows
-      const bool any = __any(nv > 0);
-      if (!any) continue;
-      f32x4_t st[4];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        st[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          U4 ka;
-          ka.u = *(const u32x4_t*)(&Ks[(kb * 16 + c16) * KSTR + ks * 32 + q4 * 8]);
-          st[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka.v, qf[gi][ks].v, st[kb], 0, 0, 0);
-        }
-      }
-      float mt = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float sv = kb * 16 + 4 * q4 + e < nv ? st[kb][e] * scale : -INFINITY;
-          st[kb][e] = sv;
-          mt = fmaxf(mt, sv);
-        }
-      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      const float m_new = fmaxf(m_run[gi], mt);
-      const float alpha = m_new == -INFINITY ? 1.0f : expf(m_run[gi] - m_new);
-      // p enters the PV product as the sum of two bf16 values, hi = bf16(p)
-      // and lo = bf16(p - hi) (p - hi is exact in fp32), so the product
-      // carries p to about 2^-17 relative, as an fp32 product would: no
-      // rounding of the probabilities beyond the fp32 arithmetic
-      float ls = 0.f;
-      U4 pa[2], pl[2];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float pv = kb * 16 + 4 * q4 + e < nv ? expf(st[kb][e] - m_new) : 0.f;
-          ls += pv;
-          const uint16_t hb = f2bf(pv);
-          pa[kb >> 1].h[(kb & 1) * 4 + e] = hb;
-          pl[kb >> 1].h[(kb & 1) * 4 + e] = f2bf(pv - __uint_as_float((uint32_t)hb << 16));
-        }
-      ls += __shfl_xor(ls, 16, 64);
-      ls += __shfl_xor(ls, 32, 64);
-      l_run[gi] = l_run[gi] * alpha + ls;
-      m_run[gi] = m_new;
-      // rescale O rows 4*q4 + e by their row's alpha (held by lane 4*q4 + e)
-      float al[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) al[e] = __shfl(alpha, q4 * 4 + e, 64);
-#pragma unroll
-      for (int db = 0; db < 8; ++db)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[gi][db][e] *= al[e];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-#pragma unroll
-        for (int db = 0; db < 8; ++db) {
-          const bf16_t* vr = &Vt[(db * 16 + c16) * VSTR + 32 * j + 4 * q4];
-          U4 vb;
-          const u32x2_t lo = *(const u32x2_t*)vr;
-          const u32x2_t hi = *(const u32x2_t*)(vr + 16);
-          vb.u = u32x4_t{lo.x, lo.y, hi.x, hi.y};
-          o[gi][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[j].v, vb.v, o[gi][db], 0, 0, 0);
-          o[gi][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl[j].v, vb.v, o[gi][db], 0, 0, 0);
-        }
-      }
-    }
+    for (int gi = 0; gi < 2; ++gi)
+      if (gon[gi]) group_tile(Ks, Vt, t0, F[gi], qf[gi], o[gi], m_run[gi], l_run[gi], c16, q4, scale);
     __syncthreads();
   }
-
-  // partials: (m, l) from the lane holding the row, O rows 4*q4 + e
 #pragma unroll
   for (int gi = 0; gi < 2; ++gi) {
-    if (!gon[gi]) continue;
     const int g = wave + 4 * gi;
-    if (lane < 16) {
-      const int rl = g * 16 + c16;
-      if (rl < nrows) {
-        float* pm = a.part_ml + (((size_t)split * a.rows + row0 + rl) * a.H + h) * 2;
-        pm[0] = m_run[gi];
-        pm[1] = l_run[gi];
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int rl = g * 16 + q4 * 4 + e;
-      if (rl >= nrows) continue;
-      float* po = a.part_o + (((size_t)split * a.rows + row0 + rl) * a.H + h) * 128;
-#pragma unroll
-      for (int db = 0; db < 8; ++db) po[db * 16 + c16] = o[gi][db][e];
-    }
+    if (gon[gi]) group_store(a, split, h, row0 + g * 16, min(16, nrows - g * 16), o[gi], m_run[gi],
+                             l_run[gi], lane);
   }
 }
 

@@ -184,3 +184,4 @@ def test_attention_verification_row_equals_ar_query(P):
                               B.LA_BF16, ws, None)
         torch.cuda.synchronize()
         assert torch.equal(out1[0], out[r]), (r, g, i)
+
