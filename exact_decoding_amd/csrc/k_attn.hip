@@ -145,13 +145,74 @@ struct TailLds {
   T vs[TT * VSTRIDE] __attribute__((aligned(16)));
 };
 
+// The MFMA kernel's (m, l, o) partials of the chunks of [0, F), merged in
+// chunk order with NPRE chunks' loads in flight, then the row's own part;
+// the normalised result goes to the output.
+template <int HD>
+struct PartRing {
+  static constexpr int NPRE = 8;
+  static constexpr int DPL = HD >= 64 ? HD / 64 : 1;  // output dims per lane
+  float pm[NPRE], pl[NPRE], po[NPRE][DPL];
+};
+
+template <int HD>
+__device__ __forceinline__ void ring_load(const AttnDesc& a, int h, int r, int nch, int sp, int i,
+                                          PartRing<HD>& R, int d0, bool down) {
+  if (sp < nch) {
+    const size_t pb = ((size_t)sp * a.rows + r) * a.H + h;
+    R.pm[i] = a.part_ml[pb * 2];
+    R.pl[i] = a.part_ml[pb * 2 + 1];
+#pragma unroll
+    for (int j = 0; j < PartRing<HD>::DPL; ++j) R.po[i][j] = down ? a.part_o[pb * HD + d0 + j] : 0.f;
+  }
+}
+
+// (m, l, oo) <- (m, l, oo) merged with a state (ms, ls, os)
+template <int DPL>
+__device__ __forceinline__ void ml_merge(float& m, float& l, float (&oo)[DPL], float ms, float ls,
+                                         const float (&os)[DPL]) {
+  const float mn = fmaxf(m, ms);
+  const float ca = m == -INFINITY ? 0.f : expf(m - mn);
+  const float cb = expf(ms - mn);
+  l = l * ca + ls * cb;
+#pragma unroll
+  for (int j = 0; j < DPL; ++j) oo[j] = oo[j] * ca + os[j] * cb;
+  m = mn;
+}
+
+template <typename T, int HD>
+__device__ __forceinline__ void merge_out(const AttnDesc& a, int h, int r, int nch, float m_run,
+                                          float l_run, const float (&o)[PartRing<HD>::DPL],
+                                          PartRing<HD>& R, int d0, bool down) {
+  constexpr int NPRE = PartRing<HD>::NPRE, DPL = PartRing<HD>::DPL;
+  float m = -INFINITY, l = 0.f, oo[DPL];
+#pragma unroll
+  for (int j = 0; j < DPL; ++j) oo[j] = 0.f;
+  for (int sp0 = 0; sp0 < nch; sp0 += NPRE) {
+#pragma unroll
+    for (int i = 0; i < NPRE; ++i) {
+      if (sp0 + i < nch) {
+        ml_merge<DPL>(m, l, oo, R.pm[i], R.pl[i], R.po[i]);
+        ring_load<HD>(a, h, r, nch, sp0 + i + NPRE, i, R, d0, down);
+      }
+    }
+  }
+  ml_merge<DPL>(m, l, oo, m_run, l_run, o);
+  T* out = (T*)a.out + (size_t)r * a.H * HD + h * HD;
+  const float inv = 1.0f / l;
+  if (down)
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) st_f(out + d0 + j, oo[j] * inv);
+}
+
 // The per-row part of row r, head h, by one wave (all 64 lanes) on its own
-// TailLds; writes the row's normalised output.
+// TailLds, then the merge with the MFMA partials; writes the row's
+// normalised output.
 template <typename T, int HD>
 __device__ __forceinline__ void tail_row(const AttnDesc& a, int h, int r, TailLds<T, HD>& L) {
   constexpr int NV = HD * (int)sizeof(T) / 16;       // 16-byte words per K / V row
   constexpr int NH = NV / 2;                         // words per half row (one lane)
-  constexpr int DPL = HD >= 64 ? HD / 64 : 1;        // output dims per lane (contiguous)
+  constexpr int DPL = PartRing<HD>::DPL;             // output dims per lane (contiguous)
   constexpr int VSTRIDE = TailLds<T, HD>::VSTRIDE;
   static_assert(NV % 2 == 0, "a lane holds half a row");
   float* qs = L.qs;
@@ -179,23 +240,12 @@ __device__ __forceinline__ void tail_row(const AttnDesc& a, int h, int r, TailLd
 #pragma unroll
   for (int j = 0; j < DPL; ++j) o[j] = 0.f;
 
-  // the MFMA kernel's partials of the chunks of [0, F), merged in chunk
-  // order; NPRE of them are in flight at a time, the first NPRE loaded now so
-  // their latency overlaps the tile below
-  constexpr int NPRE = 8;
+  // the first NPRE chunk partials, loaded now so their latency overlaps the
+  // tile below
   const int nch = a.mfma ? attn_nchunks(F) : 0;
-  float pm[NPRE], pl[NPRE], po[NPRE][DPL];
-  auto load_part = [&](int sp, int i) __attribute__((always_inline)) {
-    if (sp < nch) {
-      const size_t pb = ((size_t)sp * a.rows + r) * a.H + h;
-      pm[i] = a.part_ml[pb * 2];
-      pl[i] = a.part_ml[pb * 2 + 1];
+  PartRing<HD> R;
 #pragma unroll
-      for (int j = 0; j < DPL; ++j) po[i][j] = down ? a.part_o[pb * HD + d0 + j] : 0.f;
-    }
-  };
-#pragma unroll
-  for (int i = 0; i < NPRE; ++i) load_part(i, i);
+  for (int i = 0; i < PartRing<HD>::NPRE; ++i) ring_load<HD>(a, h, r, nch, i, i, R, d0, down);
   for (int i = lane; i < HD; i += 64) qs[i] = ld_f(q + i);
 
   // tiles of TT positions over [F, pos]
@@ -257,42 +307,7 @@ __device__ __forceinline__ void tail_row(const AttnDesc& a, int h, int r, TailLd
     wave_lds_sync();
   }
 
-  // merge: the MFMA chunks of [0, F) in chunk order, then this row's part
-  float m = -INFINITY, l = 0.f, oo[DPL];
-#pragma unroll
-  for (int j = 0; j < DPL; ++j) oo[j] = 0.f;
-  auto merge = [&](float ms, float lsum, const float (&os)[DPL]) __attribute__((always_inline)) {
-    const float mn = fmaxf(m, ms);
-    const float ca = m == -INFINITY ? 0.f : expf(m - mn);
-    const float cb = expf(ms - mn);
-    l = l * ca + lsum * cb;
-    if (down)
-#pragma unroll
-      for (int j = 0; j < DPL; ++j) oo[j] = oo[j] * ca + os[j] * cb;
-    m = mn;
-  };
-  for (int sp0 = 0; sp0 < nch; sp0 += NPRE) {
-#pragma unroll
-    for (int i = 0; i < NPRE; ++i) {
-      if (sp0 + i < nch) {
-        merge(pm[i], pl[i], po[i]);
-        load_part(sp0 + i + NPRE, i);
-      }
-    }
-  }
-  {
-    const float mn = fmaxf(m, m_run);
-    const float ca = m == -INFINITY ? 0.f : expf(m - mn);
-    const float cb = expf(m_run - mn);
-    l = l * ca + l_run * cb;
-#pragma unroll
-    for (int j = 0; j < DPL; ++j) oo[j] = oo[j] * ca + o[j] * cb;
-  }
-  T* out = (T*)a.out + (size_t)r * a.H * HD + h * HD;
-  const float inv = 1.0f / l;
-  if (down)
-#pragma unroll
-    for (int j = 0; j < DPL; ++j) st_f(out + d0 + j, oo[j] * inv);
+  merge_out<T, HD>(a, h, r, nch, m_run, l_run, o, R, d0, down);
 }
 
 template <typename T, int HD>
