@@ -172,3 +172,44 @@ def test_sampling_argument_checks(micro):
         gm.session(MICRO_PROMPT, 3, 3, 3, 4, temperature=-1.0)
     with pytest.raises(B.LaError):
         gm.session(MICRO_PROMPT, 3, 3, 3, 4, temperature=float("inf"))
+
+
+@pytest.mark.parametrize("N,W,G", [(2, 3, 3), (3, 0, 3), (3, 3, 0), (5, 2, 6)])
+def test_micro_sampling_edge_configs_match_oracle(micro, N, W, G):
+    """Degenerate and uneven configurations: one-token n-grams, no window,
+    no candidates, more candidates than window columns."""
+    s, w, gm, om = micro
+    compared = 0
+    for seed in range(3):
+        print(f"micro sampling N={N} W={W} G={G} seed={seed}", flush=True)
+        win = synth.gen_window(N, W, s.vocab, seed=200 + seed) if W else None
+        ref = la.lookahead(om, MICRO_PROMPT, N, W, G, 12, win if W else np.zeros((N - 1, 0)),
+                           prompt_ref=True, temperature=1.3, seed=seed)
+        ses = gm.session(MICRO_PROMPT, N, W, G, 12, window=win, prompt_ref=True,
+                         temperature=1.3, seed=seed)
+        toks = ses.decode()
+        compared += _decided_prefix(ref, ses.per_step, toks)
+        ses.close()
+    assert compared >= 6
+
+
+def test_micro_sampling_budget_and_eos(micro):
+    s, w, gm, om = micro
+    N, W, G = 3, 3, 3
+    win = synth.gen_window(N, W, s.vocab, seed=7)
+    ref = la.lookahead(om, MICRO_PROMPT, N, W, G, 7, win, prompt_ref=True, temperature=1.0, seed=5)
+    ses = gm.session(MICRO_PROMPT, N, W, G, 7, window=win, prompt_ref=True, temperature=1.0,
+                     seed=5)
+    toks = ses.decode()
+    ses.close()
+    assert len(toks) == 7
+    if min(ref.margins) >= TOL:
+        assert toks == ref.tokens
+        # stop after the first emission of the stream's third token
+        eos = ref.tokens[2]
+        ref2 = la.lookahead(om, MICRO_PROMPT, N, W, G, 7, win, prompt_ref=True,
+                            temperature=1.0, seed=5, eos_id=eos)
+        ses = gm.session(MICRO_PROMPT, N, W, G, 7, window=win, prompt_ref=True,
+                         temperature=1.0, seed=5, eos_id=eos)
+        assert ses.decode() == ref2.tokens and ref2.tokens[-1] == eos
+        ses.close()
