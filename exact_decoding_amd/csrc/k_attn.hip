@@ -549,81 +549,113 @@ __global__ __launch_bounds__(256) void k_attn_bulk(AttnDesc a) {
   }
 }
 
-// RMSNorm: y = x / sqrt(mean(x^2) + eps) * g, one workgroup per row, fixed
-// reduction order.
+// RMSNorm: y = x / sqrt(mean(x^2) + eps) * g, one workgroup per row; each
+// thread adds the squares of its 4-column groups in order, then the sums
+// are added by a fixed shuffle tree per wave and the 4 wave sums in order.
 template <typename T>
 __global__ __launch_bounds__(256) void k_rmsnorm(const float* x, const T* g, T* y, int d,
                                                  float eps) {
-  __shared__ float red[256];
-  const int m = blockIdx.x, tid = threadIdx.x;
+  __shared__ float red[4];
+  const int m = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const float* xr = x + (size_t)m * d;
   float ss = 0.f;
-  for (int i = tid; i < d; i += 256) ss = fmaf(xr[i], xr[i], ss);
-  red[tid] = ss;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (tid < s) red[tid] += red[tid + s];
-    __syncthreads();
+  for (int i = tid * 4; i < d; i += 1024) {
+    const float4 v = *(const float4*)(xr + i);
+    ss = fmaf(v.x, v.x, ss);
+    ss = fmaf(v.y, v.y, ss);
+    ss = fmaf(v.z, v.z, ss);
+    ss = fmaf(v.w, v.w, ss);
   }
-  const float rs = 1.0f / sqrtf(red[0] / (float)d + eps);
+  ss = wave_sum(ss);
+  if (lane == 0) red[wv] = ss;
+  __syncthreads();
+  const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+  const float rs = 1.0f / sqrtf(tot / (float)d + eps);
   T* yr = y + (size_t)m * d;
-  for (int i = tid; i < d; i += 256) st_f(yr + i, xr[i] * rs * ld_f(g + i));
+  for (int i = tid * 4; i < d; i += 1024) {
+    const float4 v = *(const float4*)(xr + i);
+    st_f(yr + i, v.x * rs * ld_f(g + i));
+    st_f(yr + i + 1, v.y * rs * ld_f(g + i + 1));
+    st_f(yr + i + 2, v.z * rs * ld_f(g + i + 2));
+    st_f(yr + i + 3, v.w * rs * ld_f(g + i + 3));
+  }
+}
+
+// Embedding gather to the fp32 residual stream, eight columns per thread.
+__device__ __forceinline__ void ld8(const bf16_t* p, float (&v)[8]) {
+  const u32x4_t u = *(const u32x4_t*)p;
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[2 * e] = __uint_as_float(w[e] << 16);
+    v[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ void ld8(const float* p, float (&v)[8]) {
+  const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
 template <typename T>
 __global__ __launch_bounds__(256) void k_embed(const int32_t* ids, const T* emb, float* x, int d) {
   const int m = blockIdx.x;
   const T* e = emb + (size_t)ids[m] * d;
-  for (int i = threadIdx.x; i < d; i += 256) x[(size_t)m * d + i] = ld_f(e + i);
+  float* xr = x + (size_t)m * d;
+  for (int i = threadIdx.x * 8; i < d; i += 2048) {
+    float v[8];
+    ld8(e + i, v);
+    *(float4*)(xr + i) = make_float4(v[0], v[1], v[2], v[3]);
+    *(float4*)(xr + i + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  }
 }
 
 // Row argmax with ties to the lowest id: the winner is the maximum of
-// (value, -id), which no reduction order can change.
-__global__ __launch_bounds__(256) void k_argmax(const float* logits, int V, int32_t* out) {
-  __shared__ float sv[256];
-  __shared__ int si[256];
-  const int m = blockIdx.x, tid = threadIdx.x;
+// (value, -id), which no reduction order can change.  1024 threads per row,
+// eight independent chains per thread, then shuffle and LDS combines.
+__device__ __forceinline__ void amax_take(float& bv, int& bi, float v, int i) {
+  if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
+}
+
+__global__ __launch_bounds__(1024) void k_argmax(const float* logits, int V, int32_t* out) {
+  __shared__ float sv[16];
+  __shared__ int si[16];
+  const int m = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const float* row = logits + (size_t)m * V;
-  // eight independent (value, index) chains per thread, combined in order
   float bv8[8];
   int bi8[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) { bv8[u] = -INFINITY; bi8[u] = 0x7fffffff; }
   int n0 = tid;
-  for (; n0 + 7 * 256 < V; n0 += 8 * 256) {
+  for (; n0 + 7 * 1024 < V; n0 += 8 * 1024) {
     float v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = row[n0 + u * 256];
+    for (int u = 0; u < 8; ++u) v[u] = row[n0 + u * 1024];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (v[u] > bv8[u]) { bv8[u] = v[u]; bi8[u] = n0 + u * 256; }
+    for (int u = 0; u < 8; ++u) amax_take(bv8[u], bi8[u], v[u], n0 + u * 1024);
   }
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    if (n0 + u * 256 < V) {
-      const float v = row[n0 + u * 256];
-      if (v > bv8[u]) { bv8[u] = v; bi8[u] = n0 + u * 256; }
-    }
-  }
+  for (int u = 0; u < 8; ++u)
+    if (n0 + u * 1024 < V) amax_take(bv8[u], bi8[u], row[n0 + u * 1024], n0 + u * 1024);
   float bv = bv8[0];
   int bi = bi8[0];
 #pragma unroll
-  for (int u = 1; u < 8; ++u)
-    if (bv8[u] > bv || (bv8[u] == bv && bi8[u] < bi)) { bv = bv8[u]; bi = bi8[u]; }
-  sv[tid] = bv;
-  si[tid] = bi;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (tid < s) {
-      const float v2 = sv[tid + s];
-      const int i2 = si[tid + s];
-      if (v2 > sv[tid] || (v2 == sv[tid] && i2 < si[tid])) { sv[tid] = v2; si[tid] = i2; }
-    }
-    __syncthreads();
+  for (int u = 1; u < 8; ++u) amax_take(bv, bi, bv8[u], bi8[u]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float v2 = __shfl_xor(bv, o, 64);
+    const int i2 = __shfl_xor(bi, o, 64);
+    amax_take(bv, bi, v2, i2);
   }
-  if (tid == 0) out[m] = si[0];
+  if (lane == 0) { sv[wv] = bv; si[wv] = bi; }
+  __syncthreads();
+  if (tid == 0) {
+    float b = sv[0];
+    int i = si[0];
+    for (int w = 1; w < 16; ++w) amax_take(b, i, sv[w], si[w]);
+    out[m] = i;
+  }
 }
-
 
 }  // namespace
 
@@ -687,6 +719,6 @@ hipError_t launch_embed(const int32_t* ids, const void* emb, float* x, int rows,
 }
 
 hipError_t launch_argmax(const float* logits, int rows, int V, int32_t* out, hipStream_t st) {
-  hipLaunchKernelGGL(k_argmax, dim3(rows), dim3(256), 0, st, logits, V, out);
+  hipLaunchKernelGGL(k_argmax, dim3(rows), dim3(1024), 0, st, logits, V, out);
   return hipGetLastError();
 }

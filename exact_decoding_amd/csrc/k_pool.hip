@@ -430,8 +430,12 @@ __global__ __launch_bounds__(SV_T) void k_sample_verify(StepIO io, RowLayout L) 
   }
 }
 
+// Copy the committed block rows' K and V into the cache, 16 bytes per
+// thread and step (a 16-byte piece never crosses a head: hd is a multiple
+// of 8).
 template <typename T>
 __global__ __launch_bounds__(256) void k_kv_commit(KvCommit c) {
+  constexpr int EP = 16 / (int)sizeof(T);  // elements per 16-byte piece
   const int l = blockIdx.x, j = blockIdx.y;
   const int n = c.st->commit_n;
   if (j >= n) return;
@@ -442,11 +446,11 @@ __global__ __launch_bounds__(256) void k_kv_commit(KvCommit c) {
   const T* vb = (const T*)c.vb + ((size_t)l * c.M + row) * nk;
   T* kc = (T*)c.kc + (size_t)l * c.Hkv * c.ld_ctx * c.hd;
   T* vc = (T*)c.vc + (size_t)l * c.Hkv * c.ld_ctx * c.hd;
-  for (int u = threadIdx.x; u < nk; u += blockDim.x) {
+  for (int u = threadIdx.x * EP; u < nk; u += blockDim.x * EP) {
     const int kvh = u / c.hd, i = u - kvh * c.hd;
     const size_t dst = ((size_t)kvh * c.ld_ctx + p) * c.hd + i;
-    kc[dst] = kb[u];
-    vc[dst] = vb[u];
+    *(u32x4_t*)(kc + dst) = *(const u32x4_t*)(kb + u);
+    *(u32x4_t*)(vc + dst) = *(const u32x4_t*)(vb + u);
   }
 }
 
