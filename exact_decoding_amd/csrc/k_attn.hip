@@ -611,12 +611,15 @@ __global__ __launch_bounds__(256) void k_embed(const int32_t* ids, const T* emb,
 }
 
 // Row argmax with ties to the lowest id: the winner is the maximum of
-// (value, -id), which no reduction order can change.  1024 threads per row,
-// eight independent chains per thread, then shuffle and LDS combines.
+// (value, -id), which no reduction order can change.  1024 threads per row;
+// with V a multiple of 4 each thread reads 16-byte groups (a 32000-entry row
+// in one pass), eight independent chains per thread, then shuffle and LDS
+// combines.
 __device__ __forceinline__ void amax_take(float& bv, int& bi, float v, int i) {
   if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
 }
 
+template <bool VEC>
 __global__ __launch_bounds__(1024) void k_argmax(const float* logits, int V, int32_t* out) {
   __shared__ float sv[16];
   __shared__ int si[16];
@@ -626,17 +629,31 @@ __global__ __launch_bounds__(1024) void k_argmax(const float* logits, int V, int
   int bi8[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) { bv8[u] = -INFINITY; bi8[u] = 0x7fffffff; }
-  int n0 = tid;
-  for (; n0 + 7 * 1024 < V; n0 += 8 * 1024) {
-    float v[8];
+  if (VEC) {
+    const int ng = V / 4;
+    for (int g0 = tid; g0 < ng; g0 += 8 * 1024) {
+      float4 v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = row[n0 + u * 1024];
+      for (int u = 0; u < 8; ++u)
+        if (g0 + u * 1024 < ng) v[u] = *(const float4*)(row + 4 * (g0 + u * 1024));
 #pragma unroll
-    for (int u = 0; u < 8; ++u) amax_take(bv8[u], bi8[u], v[u], n0 + u * 1024);
+      for (int u = 0; u < 8; ++u) {
+        const int i = 4 * (g0 + u * 1024);
+        if (g0 + u * 1024 < ng) {
+          amax_take(bv8[u], bi8[u], v[u].x, i);
+          amax_take(bv8[u], bi8[u], v[u].y, i + 1);
+          amax_take(bv8[u], bi8[u], v[u].z, i + 2);
+          amax_take(bv8[u], bi8[u], v[u].w, i + 3);
+        }
+      }
+    }
+  } else {
+    for (int n0 = tid; n0 < V; n0 += 8 * 1024) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (n0 + u * 1024 < V) amax_take(bv8[u], bi8[u], row[n0 + u * 1024], n0 + u * 1024);
+    }
   }
-#pragma unroll
-  for (int u = 0; u < 8; ++u)
-    if (n0 + u * 1024 < V) amax_take(bv8[u], bi8[u], row[n0 + u * 1024], n0 + u * 1024);
   float bv = bv8[0];
   int bi = bi8[0];
 #pragma unroll
@@ -719,6 +736,9 @@ hipError_t launch_embed(const int32_t* ids, const void* emb, float* x, int rows,
 }
 
 hipError_t launch_argmax(const float* logits, int rows, int V, int32_t* out, hipStream_t st) {
-  hipLaunchKernelGGL(k_argmax, dim3(rows), dim3(1024), 0, st, logits, V, out);
+  if (V % 4 == 0)
+    hipLaunchKernelGGL(k_argmax<true>, dim3(rows), dim3(1024), 0, st, logits, V, out);
+  else
+    hipLaunchKernelGGL(k_argmax<false>, dim3(rows), dim3(1024), 0, st, logits, V, out);
   return hipGetLastError();
 }

@@ -213,3 +213,20 @@ def test_bf16_near_maximum_rows_bit_exact():
     ar_ses.close()
     gm.close()
     assert la_toks == ar_toks
+
+
+def test_vocab_not_multiple_of_four_matches_oracle():
+    """A vocabulary of 253 ids takes the argmax's scalar path."""
+    import dataclasses
+    s = dataclasses.replace(synth.SHAPES["tiny"], name="tiny_v253", vocab=253)
+    w = synth.gen_weights(s, 0)
+    gm, om = Model(s, w), OracleModel(s, w)
+    prompt = synth.prompt_motif(s.vocab, seed=4)
+    N, W, G = 3, 4, 4
+    win = synth.gen_window(N, W, s.vocab, seed=5)
+    print("tiny vocab 253", flush=True)
+    ar = la.greedy_ar(om, prompt, 16)
+    ses = gm.session(prompt, N, W, G, 16, window=win, prompt_ref=True)
+    assert ses.decode() == ar.tokens
+    ses.close()
+    gm.close()
