@@ -28,6 +28,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+METRIC = "batch-1 greedy tokens/sec at 7B shape (N=5,W=15,G=15); step compression; HBM GB/s"
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
@@ -238,11 +239,16 @@ def main():
     log(f"[bench] generating + uploading {shape.name} weights")
     weights_np = []
     dev = []
-    for i in range(len(synth.weight_names(shape))):
+    n_w = len(synth.weight_names(shape))
+    t_log = time.time()
+    for i in range(n_w):
         w = synth.gen_tensor(shape, 0, i)
         dev.append(upload(w))
         if args.cpu_baseline == "on":
             weights_np.append(w)
+        if time.time() - t_log > 30:
+            t_log = time.time()
+            log(f"[bench] {i + 1}/{n_w} tensors after {t_log - t0:.0f}s")
     torch.cuda.synchronize()
     log(f"[bench] weights ready in {time.time() - t0:.1f}s")
     model = Model(shape, dev)
@@ -348,7 +354,9 @@ def main():
         log(f"[bench] cpu baseline: {cpu}")
 
     out = {
-        "metric": "batch-1 greedy tokens/sec at 7B shape (N=5,W=15,G=15); step compression; HBM GB/s",
+        "metric": METRIC if (shape.name, N, W, G) == ("llama7b", 5, 15, 15) else
+                  f"batch-1 greedy tokens/sec at {shape.name} shape (N={N},W={W},G={G}); "
+                  f"step compression; HBM GB/s",
         "value": la_tps, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if shape.dtype == "bf16" else "f32", "data": "synthetic",
