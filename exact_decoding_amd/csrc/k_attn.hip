@@ -679,7 +679,7 @@ __global__ __launch_bounds__(1024) void k_argmax(const float* logits, int V, int
 int attn_uses_mfma(int dtype, int hd) { return dtype == LA_BF16 && hd == 128; }
 
 size_t attn_part_floats(int nsplit, int rows, int H, int hd) {
-  return (size_t)nsplit * rows * H * (hd + 2) + (size_t)rows * H * (hd + 2);
+  return (size_t)nsplit * rows * H * (hd + 2);
 }
 
 hipError_t launch_attention(const AttnDesc& a, int dtype, hipStream_t st) {

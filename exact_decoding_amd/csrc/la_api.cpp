@@ -357,8 +357,6 @@ int enqueue_forward(la_session* ss, int rows, bool mode_prefill) {
     if (a.mfma) {
       a.part_o = ss->at<float>(ss->v.att_part);
       a.part_ml = a.part_o + (size_t)a.nsplit * rows * s.H * s.hd;
-      a.tail_o = a.part_ml + (size_t)a.nsplit * rows * s.H * 2;
-      a.tail_ml = a.tail_o + (size_t)rows * s.H * s.hd;
     }
     LA_KP(LA_PROF_ATTN, att_bytes, att_flops, launch_attention(a, dt, st), "attention");
     LA_K(trace_copy(ss, att, qrow), "trace");
@@ -816,8 +814,6 @@ int la_kernel_attention(const void* q, const void* k_cache, const void* v_cache,
     if (!ws || ws_bytes < need) return fail(LA_ENOMEM, "attention workspace too small");
     a.part_o = (float*)ws;
     a.part_ml = a.part_o + (size_t)a.nsplit * M * H * hd;
-    a.tail_o = a.part_ml + (size_t)a.nsplit * M * H * 2;
-    a.tail_ml = a.tail_o + (size_t)M * H * hd;
   }
   LA_HIP(launch_attention(a, dtype, (hipStream_t)hip_stream));
   return LA_OK;

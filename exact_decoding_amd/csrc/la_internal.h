@@ -160,8 +160,6 @@ struct AttnDesc {
   int nsplit;          // chunks allocated in part_* (grid of the MFMA kernel)
   float* part_o;       // [nsplit][rows][H][hd] unnormalised outputs
   float* part_ml;      // [nsplit][rows][H][2] running max, sum
-  float* tail_o;       // [rows][H][hd]
-  float* tail_ml;      // [rows][H][2]
 };
 hipError_t launch_attention(const AttnDesc& a, int dtype, hipStream_t st);
 // Whether the MFMA kernel takes the shared prefix (bf16, head_dim 128).
