@@ -61,6 +61,7 @@ class OracleModel:
     # have to exist at once.  Both compute the same products.
     keep = True
     BLOCK = 2048
+    on_layer = None  # optional progress callback, called with each finished layer
 
     def w(self, i: int) -> np.ndarray:
         if i in self._cache:
@@ -221,6 +222,8 @@ class OracleModel:
                 kk, vv = k, v
             x = self.attn_residual(x, self.attend(q, kk, vv, vis), li)
             x = self.mlp_residual(x, self.mlp_act(self.mlp_norm(x, li), li), li)
+            if self.on_layer is not None:
+                self.on_layer(li)
         return self.lm_head(self.final_norm(x)), new_kv
 
 

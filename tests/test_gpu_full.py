@@ -23,8 +23,6 @@ For each model:
 The oracle runs on a short prompt prefix (its cost grows with the prefix
 length), at the full layer count and width.
 """
-import time
-
 import numpy as np
 import pytest
 
@@ -37,13 +35,10 @@ from oracle import lookahead as la
 from oracle.attention import lookahead_attention
 from oracle.lookahead import block_mask, n_rows, row_offset
 from oracle.model import OracleModel, bf16_round, decode_bf16
+from progress import log as _log, ticker
 
 pytestmark = pytest.mark.gpu
 DRIFT_FACTOR = 4.0
-
-
-def _log(msg):
-    print(f"[{time.strftime('%H:%M:%S')}] {msg}", flush=True)
 
 
 def _build(name):
@@ -70,6 +65,7 @@ def _oracle_check(s, w, gm, prompt, n_new, N):
     toks, lg = _ar_logits(gm, prompt, n_new, N)
     om = OracleModel(s, w)
     om.keep = False
+    om.on_layer = ticker(s.name)
     seq = np.concatenate([np.asarray(prompt, np.int64), np.array(toks[:-1], np.int64)])
     _log(f"{s.name}: oracle teacher-forced scoring over {len(seq)} tokens (float64)")
     ref = la.score(om, seq)[len(prompt) - 1:]
