@@ -57,9 +57,12 @@ def parse():
                     help="instead of the benchmark line: step time against the row count "
                          "M over a grid of (N, W = G), one JSON line per configuration")
     ap.add_argument("--sweep-steps", type=int, default=32)
-    ap.add_argument("--calibrate", action="store_true",
-                    help="first run a 1 GiB HBM read (la_probe_read) and a 1 GiB fill, "
-                         "the known-size kernels that scale the PMC byte counters")
+    ap.add_argument("--calibrate", choices=["on", "off"], nargs="?", const="on", default="on",
+                    help="first run a 1 GiB HBM read (la_probe_read): the achievable read "
+                         "bandwidth the fractions are also reported against, and the "
+                         "known-size kernel that scales the PMC byte counters")
+    ap.add_argument("--seed-sweep", type=int, default=5,
+                    help="also report S over this many prompt seeds (0 = off)")
     return ap.parse_args()
 
 
@@ -232,7 +235,7 @@ def main():
     shape = synth.SHAPES[args.shape]
     N, W, G = args.N, args.W, args.G
     read_gbps = None
-    if args.calibrate:
+    if args.calibrate == "on":
         read_gbps = calibrate()
         log(f"[bench] calibration: 1 GiB read at {read_gbps:.0f} GB/s")
     t0 = time.time()
@@ -308,6 +311,32 @@ def main():
     # (with sampling the two streams are different draws of one distribution)
     exact = ar_tokens_ref == la_tokens_ref if args.temperature == 0 else None
 
+    # prefill of the prompt alone (eager session set-up: no graph capture)
+    t_pf = []
+    for _ in range(3):
+        sync()
+        t1 = time.perf_counter()
+        ses = model.session(prompt, N, W, G, args.max_new, window=window, prompt_ref=True,
+                            graph=False)
+        sync()
+        t_pf.append((time.perf_counter() - t1) * 1e3)
+        ses.close()
+    prefill_ms = sorted(t_pf)[1]
+    log(f"[bench] prefill of {len(prompt)} tokens: {prefill_ms:.2f} ms")
+
+    # step compression over prompt seeds 0.. (one whole generation each)
+    S_seeds = []
+    for ps in range(args.seed_sweep):
+        pr = synth.prompt_zipf_spans(shape.vocab, length=args.prompt_len, seed=ps)
+        ses = model.session(pr, N, W, G, args.max_new, window=window, prompt_ref=True,
+                            graph=graph, temperature=args.temperature, seed=args.seed)
+        ses.decode()
+        st = ses.stats()
+        ses.close()
+        S_seeds.append(st["tokens"] / st["steps"])
+    if S_seeds:
+        log(f"[bench] S over prompt seeds 0..{args.seed_sweep - 1}: {S_seeds}")
+
     # per-kernel profile (HIP events around every launch, same stream)
     ses = la_session()
     agg = None
@@ -366,15 +395,19 @@ def main():
                    "N": N, "W": W, "G": G, "rows_per_step": M, "parallelism": "single GPU",
                    "graph": graph, "temperature": args.temperature},
         "step_compression": S,
+        "step_compression_prompt_seeds": S_seeds,
+        "prefill_ms": prefill_ms,
         "ar_tokens_per_s": ar_tps,
         "speedup_vs_ar": la_tps / ar_tps,
         "lookahead_equals_ar": exact,
         "step_hbm": {"bytes_per_step": step_bytes, "GBps": step_gbps, "frac": step_gbps / HBM_PEAK_GBPS,
+                     "frac_of_achievable": step_gbps / read_gbps if read_gbps else None,
                      "P_avg": P_avg},
         "roofline": {"kernel": "projection GEMM k_gemm4 at M = 121 (QKV, O, gate/up, down and LM head)",
                      "bound": "hbm",
                      "achieved": gemm_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": gemm_gbps / HBM_PEAK_GBPS, "traffic": gemm_traffic(),
+                     "frac_of_achievable": gemm_gbps / read_gbps if read_gbps else None,
                      "avg_launch_ms": gemm_ms, "avg_launch_bytes": gemm_bytes,
                      "mfma_tflops": g["flops"] / (g["ms"] * 1e-3) / 1e12},
         "profile_ms_per_step": breakdown,
