@@ -284,16 +284,21 @@ __device__ __forceinline__ void tail_row(const AttnDesc& a, int h, int r, TailLd
       for (int j = 0; j < DPL; ++j) acc[u][j] = 0.f;
     if (down) {
       const int n = min(TT, pos - base + 1);
+      // four keys at a time: their weights and values are read together,
+      // then key jj + u is added to partial u (keys past n leave it as is)
       for (int jj = 0; jj < n; jj += 4) {
+        const float4 w4 = *(const float4*)(ps + jj);
+        const float w[4] = {w4.x, w4.y, w4.z, w4.w};
+        float vv[4][DPL];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          if (jj + u < n) {
-            const float w = ps[jj + u];
-            const T* vrow = vs + (jj + u) * VSTRIDE + d0;
+        for (int u = 0; u < 4; ++u)
 #pragma unroll
-            for (int j = 0; j < DPL; ++j) acc[u][j] = fmaf(w, ld_f(vrow + j), acc[u][j]);
-          }
-        }
+          for (int j = 0; j < DPL; ++j) vv[u][j] = ld_f(vs + (jj + u) * VSTRIDE + d0 + j);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int j = 0; j < DPL; ++j)
+            acc[u][j] = jj + u < n ? fmaf(w[u], vv[u][j], acc[u][j]) : acc[u][j];
       }
     }
     const float mn = fmaxf(m_run, mp);
