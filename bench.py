@@ -57,6 +57,9 @@ def parse():
                     help="instead of the benchmark line: step time against the row count "
                          "M over a grid of (N, W = G), one JSON line per configuration")
     ap.add_argument("--sweep-steps", type=int, default=32)
+    ap.add_argument("--attention", action="store_true",
+                    help="instead: time the lookahead attention call alone (32 heads, head_dim 128, "
+                         "bf16) at prefixes 512, 2048, 8192 for (N, W, G) = (5, 15, 15) and (7, 7, 7)")
     ap.add_argument("--calibrate", choices=["on", "off"], nargs="?", const="on", default="on",
                     help="first run a 1 GiB HBM read (la_probe_read): the achievable read "
                          "bandwidth the fractions are also reported against, and the "
@@ -221,6 +224,56 @@ def sweep(args, model, shape, prompt):
                       "alpha": planner.PAGES_ALPHA, "f": planner.PAGES_F}), flush=True)
 
 
+def attention_bench(read_gbps):
+    """The attention call alone (both kernels) on seeded N(0, 1) bf16 data,
+    rotating over enough buffer sets that the K/V working set exceeds the
+    256 MB memory-side cache; bytes per call = the prefix K and V plus q,
+    block K/V and the output."""
+    import torch
+    from exact_decoding_amd import binding as B
+    H, hd = 32, 128
+    g = torch.Generator(device="cuda").manual_seed(7)
+    for P in (512, 2048, 8192):
+        for (N, W, G) in ((5, 15, 15), (7, 7, 7)):
+            M = 1 + (W + G) * (N - 1)
+            ld = P + 64
+            kv_set = 2 * H * ld * hd * 2
+            nset = max(4, -(-600_000_000 // kv_set))
+            sets = []
+            for _ in range(nset):
+                sets.append(tuple(torch.randn(*shp, device="cuda", generator=g).to(torch.bfloat16)
+                                  for shp in ((M, H * hd), (H, ld, hd), (H, ld, hd), (M, H * hd),
+                                              (M, H * hd))))
+            out = torch.empty(M, H * hd, device="cuda", dtype=torch.bfloat16)
+            ws = torch.empty(max(B.la_kernel_attention_ws_bytes(ld, H, hd, N, W, G, B.LA_BF16), 4),
+                             dtype=torch.uint8, device="cuda")
+
+            def run(i):
+                q, kc, vc, kb, vb = sets[i % nset]
+                B.la_kernel_attention(q, kc, vc, P, ld, kb, vb, out, H, H, hd, N, W, G, B.LA_BF16,
+                                      ws, None)
+            for i in range(2 * nset):
+                run(i)
+            torch.cuda.synchronize()
+            it = 50
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(it):
+                run(i)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / it * 1e3
+            nbytes = 16384 * P + 4 * M * H * hd * 2
+            gbps = nbytes / (us * 1e-6) / 1e9
+            print(json.dumps({"kernel": "lookahead attention (MFMA prefix part + per-row part)",
+                              "P": P, "N": N, "W": W, "G": G, "rows": M, "us_per_call": us,
+                              "bytes_per_call": nbytes, "GBps": gbps, "frac": gbps / HBM_PEAK_GBPS,
+                              "frac_of_achievable": gbps / read_gbps if read_gbps else None,
+                              "buffer_sets": nset}), flush=True)
+            del sets, out, ws
+            torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -238,6 +291,9 @@ def main():
     if args.calibrate == "on":
         read_gbps = calibrate()
         log(f"[bench] calibration: 1 GiB read at {read_gbps:.0f} GB/s")
+    if args.attention:
+        attention_bench(read_gbps)
+        return
     t0 = time.time()
     log(f"[bench] generating + uploading {shape.name} weights")
     weights_np = []

@@ -55,6 +55,16 @@ __device__ __forceinline__ int row_offset(int r, const RowLayout& L) {
   return rr % n1 + 1;
 }
 
+// e^x through the hardware base-2 exponential (v_exp_f32) of x log2(e):
+// about 1 ulp in the range the softmax uses, where the library expf spends a
+// dozen instructions on range reduction; the softmax of every attention
+// step (and of the autoregressive query it must match) uses it.
+__device__ __forceinline__ float exp_e(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504f); }
+
+// float -> bf16 bits, round to nearest even, by the hardware conversion
+// (v_cvt_pk_bf16_f32); equal to the integer rounding for finite values
+__device__ __forceinline__ uint16_t bf16_rne(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
@@ -172,8 +182,8 @@ template <int DPL>
 __device__ __forceinline__ void ml_merge(float& m, float& l, float (&oo)[DPL], float ms, float ls,
                                          const float (&os)[DPL]) {
   const float mn = fmaxf(m, ms);
-  const float ca = m == -INFINITY ? 0.f : expf(m - mn);
-  const float cb = expf(ms - mn);
+  const float ca = m == -INFINITY ? 0.f : exp_e(m - mn);
+  const float cb = exp_e(ms - mn);
   l = l * ca + ls * cb;
 #pragma unroll
   for (int j = 0; j < DPL; ++j) oo[j] = oo[j] * ca + os[j] * cb;
@@ -272,7 +282,7 @@ __device__ __forceinline__ void tail_row(const AttnDesc& a, int h, int r, TailLd
     const float other = __shfl_xor(mine, 1, 64);
     const float sc = on ? ((half ? other : mine) + (half ? mine : other)) * scale : -INFINITY;
     const float mp = wave_max(sc);
-    const float pv = on ? expf(sc - mp) : 0.f;
+    const float pv = on ? exp_e(sc - mp) : 0.f;
     if (!half) ps[slot] = pv;
     const float lp = wave_sum(half ? 0.f : pv);
     wave_lds_sync();
@@ -302,8 +312,8 @@ __device__ __forceinline__ void tail_row(const AttnDesc& a, int h, int r, TailLd
       }
     }
     const float mn = fmaxf(m_run, mp);
-    const float ca = m_run == -INFINITY ? 0.f : expf(m_run - mn);
-    const float cb = expf(mp - mn);
+    const float ca = m_run == -INFINITY ? 0.f : exp_e(m_run - mn);
+    const float cb = exp_e(mp - mn);
     l_run = l_run * ca + lp * cb;
 #pragma unroll
     for (int j = 0; j < DPL; ++j)
@@ -391,7 +401,7 @@ __device__ __forceinline__ void group_tile(const bf16_t* Ks, const bf16_t* Vt, i
   mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
   mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
   const float m_new = fmaxf(m_run, mt);
-  const float alpha = m_new == -INFINITY ? 1.0f : expf(m_run - m_new);
+  const float alpha = m_new == -INFINITY ? 1.0f : exp_e(m_run - m_new);
   // p enters the PV product as the sum of two bf16 values, hi = bf16(p)
   // and lo = bf16(p - hi) (p - hi is exact in fp32), so the product
   // carries p to about 2^-17 relative, as an fp32 product would: no
@@ -402,11 +412,11 @@ __device__ __forceinline__ void group_tile(const bf16_t* Ks, const bf16_t* Vt, i
   for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float pv = kb * 16 + 4 * q4 + e < nv ? expf(st[kb][e] - m_new) : 0.f;
+      const float pv = kb * 16 + 4 * q4 + e < nv ? exp_e(st[kb][e] - m_new) : 0.f;
       ls += pv;
-      const uint16_t hb = f2bf(pv);
+      const uint16_t hb = bf16_rne(pv);
       pa[kb >> 1].h[(kb & 1) * 4 + e] = hb;
-      pl[kb >> 1].h[(kb & 1) * 4 + e] = f2bf(pv - __uint_as_float((uint32_t)hb << 16));
+      pl[kb >> 1].h[(kb & 1) * 4 + e] = bf16_rne(pv - __uint_as_float((uint32_t)hb << 16));
     }
   ls += __shfl_xor(ls, 16, 64);
   ls += __shfl_xor(ls, 32, 64);
@@ -455,7 +465,10 @@ __device__ __forceinline__ void group_store(const AttnDesc& a, int split, int h,
   }
 }
 
-__global__ __launch_bounds__(256) void k_attn_bulk(AttnDesc a) {
+// Register budget of two waves per SIMD (two workgroups per compute unit):
+// with one, a long prefix's chunks run in five rounds over the chip, and a
+// tile's fetch latency is hidden by nothing but the workgroup's own math.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_bulk(AttnDesc a) {
   __shared__ __align__(16) bf16_t Ks[AT * KSTR];
   __shared__ __align__(16) bf16_t Vt[128 * VSTR];
   const int h = blockIdx.x, split = blockIdx.y, rb = blockIdx.z;
