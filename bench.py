@@ -278,7 +278,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              f"(this build has no multi-GPU path)", file=sys.stderr)
+              f"(the library has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch

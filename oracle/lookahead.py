@@ -9,7 +9,7 @@ update"), plus the prompt-as-reference variant ([LD] §5 Table 3 ⑨, [LDs]).
 Notation: N = n-gram length, W = window width, G = max candidates.
 The window has N-1 levels (level 0 = oldest Jacobi step) of W tokens.
 
-Readings where the pages are silent or garbled (also listed in the design doc):
+Readings where the pages are silent or garbled:
 
 R1  Row layout of one step (M = 1 + W(N-1) + G(N-1) rows):
       row 0                          = cur (last emitted token), position P

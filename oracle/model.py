@@ -2,7 +2,7 @@
 
 The pages evaluate LLaMA-2 / CodeLlama decoders ([LD] §5 "Evaluation
 Methodology") and state nothing more about the architecture, so the model is
-the textbook LLaMA decoder (reading, also in the design doc):
+the textbook LLaMA decoder (a reading of the pages):
 
     x      = E[token]
     per layer:
