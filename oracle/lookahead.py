@@ -55,6 +55,12 @@ R18 Sampling verification (Algorithm 4, [LD] §3.4 "Sampling verification"):
     one token is drawn that way from the last row.  Draw k of step s comes
     from rng.uniform(seed, s, k), k counting the draws of the step in the
     order they are used.  The lookahead branch stays greedy (argmax).
+R20 Top-K / top-P with temperature (the pages' examples of a target
+    sampling distribution, [LD] §3.4 "Sampling verification"): tokens are
+    ranked by logit, higher first, ties to the lower id; top-K keeps the
+    first K (K = 0: all); top-P then keeps the shortest leading run of the
+    kept tokens whose weight sum reaches p times their total (p = 1: all).
+    The other tokens get weight 0, and Algorithm 4 runs on what is left.
 """
 from __future__ import annotations
 
@@ -189,6 +195,34 @@ def row_weights(logits_row: np.ndarray, T: float) -> np.ndarray:
     return np.exp((l - l.max()) / T)
 
 
+def restricted_weights(logits_row: np.ndarray, T: float, top_k: int = 0,
+                       top_p: float = 1.0) -> tuple[np.ndarray, float]:
+    """row_weights with the top-K / top-P restriction of R20.  Returns (e,
+    margin): margin is the smallest distance of a cut from deciding the
+    other way, the logit gap at the top-K cut and, for top-P, the distance
+    of p times the total from the nearest running sum, relative to the
+    total (inf when nothing is cut)."""
+    l = np.asarray(logits_row, dtype=np.float64)
+    e = row_weights(l, T)
+    V = len(l)
+    order = np.lexsort((np.arange(V), -l))       # logit descending, then id ascending
+    margin = np.inf
+    n = V if top_k <= 0 else min(int(top_k), V)
+    if n < V:
+        margin = float(l[order[n - 1]] - l[order[n]])
+    if top_p < 1.0:
+        cs = np.cumsum(e[order[:n]])
+        target = top_p * cs[-1]
+        cut = int(np.searchsorted(cs, target, side="left"))
+        cut = min(cut, n - 1)
+        lo = cs[cut - 1] if cut > 0 else 0.0
+        margin = min(margin, float(min(target - lo, cs[cut] - target) / cs[-1]))
+        n = cut + 1
+    out = np.zeros_like(e)
+    out[order[:n]] = e[order[:n]]
+    return out, margin
+
+
 def draw_from(e: np.ndarray, removed: set, u: float) -> tuple[int, float]:
     """The first token v, in index order and leaving out `removed`, whose
     running weight sum reaches u * (sum of the remaining weights); returns
@@ -209,7 +243,7 @@ def draw_from(e: np.ndarray, removed: set, u: float) -> tuple[int, float]:
 
 
 def sample_verify(logits: np.ndarray, cands, N: int, base: int, T: float, seed: int,
-                  step: int):
+                  step: int, top_k: int = 0, top_p: float = 1.0):
     """Algorithm 4 over one step's block-row logits (R18).  Returns (emit,
     acc, g0, margin): the emitted tokens (acc accepted candidate tokens, then
     the drawn one), the candidate whose rows are committed, and the smallest
@@ -220,7 +254,8 @@ def sample_verify(logits: np.ndarray, cands, N: int, base: int, T: float, seed: 
     emit: list[int] = []
     margin = np.inf
     for i in range(1, N + 1):
-        e = row_weights(logits[row], T)
+        e, mr = restricted_weights(logits[row], T, top_k, top_p)
+        margin = min(margin, mr)
         z = float(e.sum())
         removed: set = set()
         zr = z
@@ -300,11 +335,12 @@ def _append(cache, new_kv, rows=None):
 
 def greedy_ar(model: OracleModel, prompt, max_new: int, eos_id: int = -1,
               keep_logits: bool = False, temperature: float = 0.0,
-              seed: int = 0) -> DecodeResult:
+              seed: int = 0, top_k: int = 0, top_p: float = 1.0) -> DecodeResult:
     """Plain autoregressive decoding ([LD] §3.4 "Mathematical
     Reformulation", the autoregressive system): y_{j+1} = argmax of the
     logits at the last position given prompt and y_1..y_j, or, with a
-    temperature, a draw from softmax(logits / T) (draw 0 of step j, R18)."""
+    temperature, a draw from softmax(logits / T) restricted by top-K / top-P
+    (draw 0 of step j, R18, R20)."""
     cache, cur = prefill(model, prompt)
     P = cache[0][0].shape[0]
     out: list[int] = []
@@ -317,9 +353,9 @@ def greedy_ar(model: OracleModel, prompt, max_new: int, eos_id: int = -1,
         cache = _append(cache, kv)
         P += 1
         if temperature > 0:
-            cur, m = draw_from(row_weights(logits[0], temperature), set(),
-                               rng.uniform(seed, len(out), 0))
-            margins.append(m)
+            e, mr = restricted_weights(logits[0], temperature, top_k, top_p)
+            cur, m = draw_from(e, set(), rng.uniform(seed, len(out), 0))
+            margins.append(min(m, mr))
         else:
             cur = int(argmax_lowest(logits)[0])
         out.append(cur)
@@ -341,7 +377,7 @@ def lookahead(model: OracleModel, prompt, N: int, W: int, G: int, max_new: int,
               init_window, prompt_ref: bool = False, pool_cap: int | None = None,
               eos_id: int = -1, keep_logits: bool = False,
               pool: NGramPool | None = None, temperature: float = 0.0,
-              seed: int = 0) -> DecodeResult:
+              seed: int = 0, top_k: int = 0, top_p: float = 1.0) -> DecodeResult:
     """Lookahead decoding, one step per loop iteration ([LD] §3.2, §3.4).
 
     Each step: select candidates for cur from the pool; run one forward
@@ -387,7 +423,7 @@ def lookahead(model: OracleModel, prompt, N: int, W: int, G: int, max_new: int,
 
         if temperature > 0:
             emit, acc, g0, m = sample_verify(logits, cands, N, base, temperature, seed,
-                                             res.steps)
+                                             res.steps, top_k, top_p)
             res.margins.append(m)
             bonus = emit[-1]
             prev_survivors = [g0]

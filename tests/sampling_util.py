@@ -34,17 +34,40 @@ def _gof(counts: dict, probs: dict, n: int, min_expected: float = 5.0) -> float:
     return stats.chisquare(obs, exp).pvalue
 
 
-def exact_ar_probs(model, prompt, k: int, T: float) -> dict:
-    """P(y_1..y_k) = product of softmax(logits / T) conditionals, every
-    continuation of the 8-token vocabulary enumerated."""
+def _restricted(l, T, top_k=0, top_p=1.0):
+    """softmax(l / T) over the top-K tokens by logit (ties to the lower id),
+    then over the shortest run of those, best first, holding a top_p share
+    of their probability; written as a plain loop over the ranked tokens."""
+    ranked = sorted(range(len(l)), key=lambda v: (-l[v], v))
+    if top_k > 0:
+        ranked = ranked[:top_k]
+    w = {v: np.exp((l[v] - l.max()) / T) for v in ranked}
+    total = sum(w.values())
+    keep, run = [], 0.0
+    for v in ranked:
+        keep.append(v)
+        run += w[v]
+        if top_p < 1.0 and run >= top_p * total:
+            break
+    p = np.zeros(len(l))
+    z = sum(w[v] for v in keep)
+    for v in keep:
+        p[v] = w[v] / z
+    return p
+
+
+def exact_ar_probs(model, prompt, k: int, T: float, top_k: int = 0, top_p: float = 1.0) -> dict:
+    """P(y_1..y_k) = product of the conditionals softmax(logits / T) (restricted
+    to top-K / top-P when asked), every continuation of the 8-token vocabulary
+    enumerated."""
     V = model.s.vocab
     out = {}
     for seq in itertools.product(range(V), repeat=k - 1):
         lg = LA.score(model, list(prompt) + list(seq))
         p = 1.0
         for j, t in enumerate(seq):
-            p *= _softmax(lg[len(prompt) - 1 + j], T)[t]
-        last = _softmax(lg[len(prompt) - 1 + k - 1], T)
+            p *= _restricted(lg[len(prompt) - 1 + j], T, top_k, top_p)[t]
+        last = _restricted(lg[len(prompt) - 1 + k - 1], T, top_k, top_p)
         for t in range(V):
             out[tuple(seq) + (t,)] = p * last[t]
     return out

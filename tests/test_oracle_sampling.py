@@ -13,7 +13,9 @@ known-answer vectors, not against its own formulas:
   * T -> 0 reduces Algorithm 4 to greedy verification (Algorithm 3);
   * lookahead decoding with sampling on an 8-token model reproduces the
     exact distribution of the first two tokens of autoregressive sampling,
-    enumerated from the model's conditionals.
+    enumerated from the model's conditionals, also under top-K / top-P;
+  * the top-K / top-P cuts on hand-worked rows (ties, shares exactly at and
+    past a boundary).
 """
 import collections
 import itertools
@@ -134,4 +136,59 @@ def test_lookahead_sampling_preserves_the_distribution(micro):
         cnt[tuple(r.tokens)] += 1
         accepted += r.accepted[0] > 0
     assert accepted > n // 10          # the rejection path was exercised
+    assert _gof(cnt, probs, n) > 1e-3
+
+
+def test_top_k_top_p_cuts_by_hand():
+    """R20 on rows worked out by hand (T = 1)."""
+    def kept(l, k=0, p=1.0):
+        e, _ = LA.restricted_weights(np.array(l, dtype=np.float64), 1.0, k, p)
+        return sorted(np.nonzero(e)[0].tolist())
+    l = [1.0, 3.0, 3.0, 2.0, 3.0]
+    assert kept(l) == [0, 1, 2, 3, 4]
+    assert kept(l, 1) == [1]                 # three-way tie for the top: lowest id
+    assert kept(l, 2) == [1, 2]
+    assert kept(l, 3) == [1, 2, 4]
+    assert kept(l, 4) == [1, 2, 3, 4]
+    assert kept(l, 9) == [0, 1, 2, 3, 4]     # K past the vocabulary keeps all
+    # probabilities 0.05, 0.5, 0.15, 0.3 (ranked 1, 3, 2, 0)
+    lp = np.log([0.05, 0.5, 0.15, 0.3])
+    assert kept(lp, 0, 0.4) == [1]           # 0.5 already holds 0.4
+    assert kept(lp, 0, 0.75) == [1, 3]       # 0.5 + 0.3
+    assert kept(lp, 0, 0.9) == [1, 2, 3]     # + 0.15
+    assert kept(lp, 0, 0.99) == [0, 1, 2, 3]
+    # top-K first, then top-P of what is left: 0.5 / (0.5 + 0.3) = 0.625
+    assert kept(lp, 2, 0.6) == [1]
+    assert kept(lp, 2, 0.7) == [1, 3]
+    # the kept weights are the unrestricted ones
+    e, _ = LA.restricted_weights(lp, 1.0, 2, 1.0)
+    assert e[1] == pytest.approx(1.0) and e[3] == pytest.approx(0.6)
+
+
+def test_restricted_ar_sampling_matches_enumeration(micro):
+    T, K, Pp = 1.5, 4, 0.8
+    probs = exact_ar_probs(micro, MICRO_PROMPT, 2, T, K, Pp)
+    assert sum(probs.values()) == pytest.approx(1.0)
+    assert sum(1 for v in probs.values() if v == 0.0) > 0      # the cut removed something
+    n = 1500
+    cnt = collections.Counter(tuple(LA.greedy_ar(micro, MICRO_PROMPT, 2, temperature=T, seed=s,
+                                                 top_k=K, top_p=Pp).tokens) for s in range(n))
+    assert all(probs[key] > 0 for key in cnt)                  # nothing outside the cut
+    assert _gof(cnt, probs, n) > 1e-3
+
+
+def test_restricted_lookahead_sampling_preserves_the_distribution(micro):
+    T, N, W, G, K, Pp = 1.5, 3, 3, 3, 4, 0.8
+    probs = exact_ar_probs(micro, MICRO_PROMPT, 2, T, K, Pp)
+    n = 1500
+    cnt = collections.Counter()
+    accepted = 0
+    for s in range(n):
+        win = synth.gen_window(N, W, micro.s.vocab, seed=100 + s)
+        r = LA.lookahead(micro, MICRO_PROMPT, N, W, G, 2, win, prompt_ref=True,
+                         temperature=T, seed=s, top_k=K, top_p=Pp)
+        cnt[tuple(r.tokens)] += 1
+        accepted += r.accepted[0] > 0
+    assert accepted > n // 10
+    assert all(probs[key] > 0 for key in cnt)
     assert _gof(cnt, probs, n) > 1e-3
