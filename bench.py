@@ -53,6 +53,8 @@ def parse():
                     help="> 0: sampling verification (Algorithm 4) at this temperature, "
                          "for lookahead and AR alike; 0: greedy")
     ap.add_argument("--seed", type=int, default=0, help="key of the sampling draws")
+    ap.add_argument("--top-k", type=int, default=0, help="sampling: top-K cut (0 = none)")
+    ap.add_argument("--top-p", type=float, default=0.0, help="sampling: top-P cut (0 = none)")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the benchmark line: step time against the row count "
                          "M over a grid of (N, W = G), one JSON line per configuration")
@@ -321,11 +323,13 @@ def main():
 
     def la_session():
         return model.session(prompt, N, W, G, args.max_new, window=window, prompt_ref=True,
-                             graph=graph, temperature=args.temperature, seed=args.seed)
+                             graph=graph, temperature=args.temperature, seed=args.seed,
+                             top_k=args.top_k, top_p=args.top_p)
 
     def ar_session():
         return model.session(prompt, N, W, G, args.max_new, ar=True, graph=graph,
-                             temperature=args.temperature, seed=args.seed)
+                             temperature=args.temperature, seed=args.seed, top_k=args.top_k,
+                             top_p=args.top_p)
 
     # warmup + steps per generation
     log("[bench] warmup")
@@ -385,7 +389,8 @@ def main():
     for ps in range(args.seed_sweep):
         pr = synth.prompt_zipf_spans(shape.vocab, length=args.prompt_len, seed=ps)
         ses = model.session(pr, N, W, G, args.max_new, window=window, prompt_ref=True,
-                            graph=graph, temperature=args.temperature, seed=args.seed)
+                            graph=graph, temperature=args.temperature, seed=args.seed,
+                            top_k=args.top_k, top_p=args.top_p)
         ses.decode()
         st = ses.stats()
         ses.close()
@@ -449,7 +454,8 @@ def main():
                                f"prompt {len(prompt)} Zipf(1.1)+3 repeated spans, prompt as reference, "
                                f"{args.max_new} new tokens per generation",
                    "N": N, "W": W, "G": G, "rows_per_step": M, "parallelism": "single GPU",
-                   "graph": graph, "temperature": args.temperature},
+                   "graph": graph, "temperature": args.temperature, "top_k": args.top_k,
+                   "top_p": args.top_p},
         "step_compression": S,
         "step_compression_prompt_seeds": S_seeds,
         "prefill_ms": prefill_ms,

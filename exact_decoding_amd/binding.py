@@ -51,7 +51,8 @@ class DecodeParams(ctypes.Structure):
                 ("pool_cap", ctypes.c_int32), ("max_ctx", ctypes.c_int32),
                 ("max_new", ctypes.c_int32), ("eos_id", ctypes.c_int32),
                 ("flags", ctypes.c_uint32), ("temperature", ctypes.c_float),
-                ("reserved", ctypes.c_uint32), ("seed", ctypes.c_uint64)]
+                ("top_k", ctypes.c_int32), ("seed", ctypes.c_uint64),
+                ("top_p", ctypes.c_float), ("reserved", ctypes.c_uint32)]
 
 
 class PoolStats(ctypes.Structure):

@@ -249,6 +249,7 @@ __global__ __launch_bounds__(SV_T) void k_sample_verify(StepIO io, RowLayout L) 
   __shared__ float e[SAMPLE_VMAX];
   __shared__ float red[SV_T];
   __shared__ float wtot[SV_T / 64];
+  __shared__ int wcnt[SV_T / 64];
   __shared__ int32_t removed[VMAX_M];
   __shared__ int32_t surv[VMAX_M];
   __shared__ int s_nrem, s_pick, s_nsurv, s_row, s_done_pos;
@@ -263,6 +264,142 @@ __global__ __launch_bounds__(SV_T) void k_sample_verify(StepIO io, RowLayout L) 
   const unsigned long long step = (unsigned long long)st->stats[ST_STEPS];
   const int ncand = st->ncand;
   uint32_t k = 0;  // draws used (same on every thread)
+
+  // Block-wide integer count and float sum, the same on every thread: a
+  // shuffle tree within each wave (each pairwise sum is symmetric, so every
+  // lane ends with the same bits), then the 16 wave totals in order.
+  auto block_count = [&](int c) -> int {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
+    if (lane == 0) wcnt[wv] = c;
+    __syncthreads();
+    int t = 0;
+    for (int w = 0; w < SV_T / 64; ++w) t += wcnt[w];
+    __syncthreads();
+    return t;
+  };
+  auto block_fsum = [&](float x) -> float {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+    if (lane == 0) wtot[wv] = x;
+    __syncthreads();
+    float t = 0.f;
+    for (int w = 0; w < SV_T / 64; ++w) t += wtot[w];
+    __syncthreads();
+    return t;
+  };
+  // exclusive prefix over the threads (vocabulary order) of x
+  auto block_exscan = [&](float x) -> float {
+    float y = x;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float t = __shfl_up(y, o, 64);
+      if (lane >= o) y += t;
+    }
+    if (lane == 63) wtot[wv] = y;
+    __syncthreads();
+    float before = 0.f;
+    for (int w = 0; w < wv; ++w) before += wtot[w];
+    __syncthreads();
+    return before + (y - x);
+  };
+  auto block_exscan_i = [&](int x) -> int {
+    int y = x;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(y, o, 64);
+      if (lane >= o) y += t;
+    }
+    if (lane == 63) wcnt[wv] = y;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wv; ++w) before += wcnt[w];
+    __syncthreads();
+    return before + (y - x);
+  };
+  // Top-K / top-P cut of e[] (the row's logits `lg`): tokens are ranked by
+  // logit, higher first, ties to the lower id.  Thresholds are found bit by
+  // bit on an order-preserving integer key of the logit; the tokens tied at
+  // the threshold are taken in id order (the thread slices are in id order).
+  auto restrict_cut = [&](const float* lg) {
+    constexpr int CHMAX = (SAMPLE_VMAX + SV_T - 1) / SV_T;
+    uint32_t kk[CHMAX];
+#pragma unroll
+    for (int j = 0; j < CHMAX; ++j) {
+      const uint32_t u = v0 + j < v1 ? __float_as_uint(lg[v0 + j]) : 0u;
+      kk[j] = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    }
+    auto in = [&](int j) { return v0 + j < v1; };
+    if (io.top_k > 0) {
+      // the top_k-th largest key: the largest t with #{key >= t} >= top_k
+      uint32_t t = 0;
+      for (int b = 31; b >= 0; --b) {
+        const uint32_t c = t | (1u << b);
+        int n = 0;
+#pragma unroll
+        for (int j = 0; j < CHMAX; ++j) n += in(j) && kk[j] >= c;
+        if (block_count(n) >= io.top_k) t = c;
+      }
+      int ngt = 0, neq = 0;
+#pragma unroll
+      for (int j = 0; j < CHMAX; ++j) {
+        ngt += in(j) && kk[j] > t;
+        neq += in(j) && kk[j] == t;
+      }
+      const int need = io.top_k - block_count(ngt);  // tied tokens kept, lowest ids
+      int seen = block_exscan_i(neq);
+#pragma unroll
+      for (int j = 0; j < CHMAX; ++j) {
+        if (!in(j)) continue;
+        if (kk[j] < t) e[v0 + j] = 0.f;
+        else if (kk[j] == t) {
+          if (seen >= need) e[v0 + j] = 0.f;
+          ++seen;
+        }
+      }
+      __syncthreads();
+    }
+    if (io.top_p < 1.f) {
+      float loc = 0.f;
+#pragma unroll
+      for (int j = 0; j < CHMAX; ++j)
+        if (in(j)) loc += e[v0 + j];
+      const float target = io.top_p * block_fsum(loc);
+      // the largest key t whose tokens at or above it hold the target
+      uint32_t t = 0;
+      for (int b = 31; b >= 0; --b) {
+        const uint32_t c = t | (1u << b);
+        float x = 0.f;
+#pragma unroll
+        for (int j = 0; j < CHMAX; ++j)
+          if (in(j) && kk[j] >= c) x += e[v0 + j];
+        if (block_fsum(x) >= target) t = c;
+      }
+      float sgt = 0.f, seq = 0.f;
+#pragma unroll
+      for (int j = 0; j < CHMAX; ++j) {
+        if (!in(j)) continue;
+        if (kk[j] > t) sgt += e[v0 + j];
+        else if (kk[j] == t) seq += e[v0 + j];
+      }
+      const float above = block_fsum(sgt);
+      float run = above + block_exscan(seq);
+      bool full = run >= target;  // the tied tokens of earlier slices reached it
+#pragma unroll
+      for (int j = 0; j < CHMAX; ++j) {
+        if (!in(j)) continue;
+        if (kk[j] < t) e[v0 + j] = 0.f;
+        else if (kk[j] == t) {
+          if (full) e[v0 + j] = 0.f;
+          else {
+            run += e[v0 + j];
+            full = run >= target;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  };
 
   // load row `row`'s weights into e[], return Z (fixed order)
   auto weights = [&](int row) -> float {
@@ -282,6 +419,11 @@ __global__ __launch_bounds__(SV_T) void k_sample_verify(StepIO io, RowLayout L) 
       const float w = expf((lg[v] - mx) / io.temp);
       e[v] = w;
       sum += w;
+    }
+    if (io.top_k > 0 || io.top_p < 1.f) {
+      restrict_cut(lg);
+      sum = 0.f;
+      for (int v = v0; v < v1; ++v) sum += e[v];
     }
     red[tid] = sum;
     __syncthreads();

@@ -180,6 +180,8 @@ int check_params(const la_model* m, const la_decode_params* p) {
   const long long M = 1 + (W + G) * (p->N - 1);
   if (M > 2048) return fail(LA_EINVAL, "1 + (W+G)(N-1) must be <= 2048");
   if (p->reserved != 0) return fail(LA_EINVAL, "reserved must be 0");
+  if (p->top_k < 0) return fail(LA_EINVAL, "top_k must be >= 0");
+  if (!(p->top_p >= 0.f && p->top_p <= 1.f)) return fail(LA_EINVAL, "top_p must be in [0, 1]");
   if (!(p->temperature >= 0.f) || !std::isfinite(p->temperature))
     return fail(LA_EINVAL, "temperature must be finite and >= 0");
   if (p->temperature > 0.f && m->d.vocab > SAMPLE_VMAX)
@@ -417,6 +419,8 @@ int enqueue_step(la_session* ss) {
   io.V = s.V;
   io.temp = ss->p.temperature;
   io.seed = (unsigned long long)ss->p.seed;
+  io.top_k = ss->p.top_k < s.V ? ss->p.top_k : 0;
+  io.top_p = ss->p.top_p > 0.f && ss->p.top_p < 1.f ? ss->p.top_p : 1.f;
 
   const double R = s.M, ES = (double)dtype_size(dt);
   LA_KP(LA_PROF_BOOK, 0, 0, launch_gather(pool, io, ss->lay, st), "gather");

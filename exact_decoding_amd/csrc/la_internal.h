@@ -205,6 +205,8 @@ struct StepIO {
   int V;
   float temp;
   unsigned long long seed;
+  int top_k;      // 0: no top-K cut (else 1 <= top_k < V)
+  float top_p;    // 1: no top-P cut (else 0 < top_p < 1)
 };
 hipError_t launch_gather(const PoolDesc& pool, const StepIO& io, const RowLayout& lay,
                          hipStream_t st);

@@ -66,15 +66,17 @@ class Model:
     def session(self, prompt, N: int, W: int, G: int, max_new: int, window=None,
                 prompt_ref: bool = False, ar: bool = False, graph: bool = True,
                 max_ctx: int | None = None, pool_cap: int = 0, eos_id: int = -1,
-                temperature: float = 0.0, seed: int = 0) -> "Session":
+                temperature: float = 0.0, seed: int = 0, top_k: int = 0,
+                top_p: float = 0.0) -> "Session":
         """temperature 0: greedy; > 0: sampling verification with draws keyed
-        by `seed` (see la.h)."""
+        by `seed`, optionally cut to the top_k tokens and then to a top_p share
+        (0 = no cut; see la.h)."""
         flags = (B.LA_PROMPT_REF if prompt_ref else 0) | (B.LA_AR if ar else 0)
         flags |= 0 if graph else B.LA_NO_GRAPH
         if max_ctx is None:
             max_ctx = len(prompt) + max_new + N + W + 2
         p = B.DecodeParams(N, W, G, pool_cap, max_ctx, max_new, eos_id, flags,
-                           float(temperature), 0, int(seed))
+                           float(temperature), int(top_k), int(seed), float(top_p), 0)
         return Session(self, p, prompt, window)
 
     def close(self):

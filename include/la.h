@@ -76,14 +76,27 @@ typedef struct {
  *              ([LD] §3.4 "Sampling verification (Algorithm 4)") against
  *              softmax(logits / temperature); the lookahead branch stays
  *              greedy.  Needs vocab <= 32768.  With LA_AR: plain sampling.
+ * top_k      with temperature > 0: only the top_k tokens by logit (ties to
+ *              the lower id) keep their weight; 0 means all, and so does a
+ *              value >= vocab.  Must be >= 0.
+ * top_p      with temperature > 0: of those, only the shortest leading run
+ *              (same order) whose weights reach top_p times their sum; 0 or
+ *              1 means no cut, otherwise 0 < top_p < 1.  top-K and top-P are
+ *              the pages' examples of a sampling target ([LD] §3.4
+ *              "Sampling verification"); Algorithm 4 runs on the cut weights.
+ *              Both are ignored when temperature is 0.
  * seed       key of the step's draws (Philox4x32-10, counter = (step, draw
- *              index); see la_philox_uniform). */
+ *              index); see la_philox_uniform).
+ * reserved   must be 0.
+ * A zero-initialised struct with N, max_ctx and max_new set is valid. */
 typedef struct {
   int32_t N, W, G, pool_cap, max_ctx, max_new, eos_id;
   uint32_t flags;
   float temperature;
-  uint32_t reserved;  /* must be 0 */
+  int32_t top_k;
   uint64_t seed;
+  float top_p;
+  uint32_t reserved;
 } la_decode_params;
 
 #define LA_PROMPT_REF 1u

@@ -59,7 +59,8 @@ R20 Top-K / top-P with temperature (the pages' examples of a target
     sampling distribution, [LD] §3.4 "Sampling verification"): tokens are
     ranked by logit, higher first, ties to the lower id; top-K keeps the
     first K (K = 0: all); top-P then keeps the shortest leading run of the
-    kept tokens whose weight sum reaches p times their total (p = 1: all).
+    kept tokens whose weight sum reaches p times their total (p = 1, or
+    0, keeps all).
     The other tokens get weight 0, and Algorithm 4 runs on what is left.
 """
 from __future__ import annotations
@@ -210,7 +211,7 @@ def restricted_weights(logits_row: np.ndarray, T: float, top_k: int = 0,
     n = V if top_k <= 0 else min(int(top_k), V)
     if n < V:
         margin = float(l[order[n - 1]] - l[order[n]])
-    if top_p < 1.0:
+    if 0.0 < top_p < 1.0:
         cs = np.cumsum(e[order[:n]])
         target = top_p * cs[-1]
         cut = int(np.searchsorted(cs, target, side="left"))

@@ -11,6 +11,11 @@
    (chi-square), with candidates accepted in most first steps.
 4. tiny fp32 (vocab 256) sampling matches the oracle while decided; a bf16
    model at T = 1e-6 emits its greedy tokens.
+5. Top-K / top-P cuts: the micro model's lookahead and AR sampling under
+   cuts match the oracle while decided (the cuts' margins included), and
+   follow the exact cut distribution over 1500 seeds; on a 4000-token bf16
+   model top-K = 1, or a vanishing top-P share, reproduces the greedy stream
+   exactly at T = 1.
 """
 import collections
 
@@ -213,3 +218,70 @@ def test_micro_sampling_budget_and_eos(micro):
                          temperature=1.0, seed=5, eos_id=eos)
         assert ses.decode() == ref2.tokens and ref2.tokens[-1] == eos
         ses.close()
+
+
+@pytest.mark.parametrize("K,Pp", [(3, 0.0), (0, 0.8), (4, 0.9)])
+def test_micro_restricted_sampling_matches_oracle(micro, K, Pp):
+    s, w, gm, om = micro
+    N, W, G, T = 3, 3, 3, 1.3
+    compared = 0
+    for seed in range(4):
+        print(f"micro top_k={K} top_p={Pp} seed={seed}", flush=True)
+        win = synth.gen_window(N, W, s.vocab, seed=300 + seed)
+        ref = la.lookahead(om, MICRO_PROMPT, N, W, G, 20, win, prompt_ref=True, temperature=T,
+                           seed=seed, top_k=K, top_p=Pp)
+        ses = gm.session(MICRO_PROMPT, N, W, G, 20, window=win, prompt_ref=True,
+                         temperature=T, seed=seed, top_k=K, top_p=Pp)
+        compared += _decided_prefix(ref, ses.per_step, ses.decode())
+        ses.close()
+        ref = la.greedy_ar(om, MICRO_PROMPT, 12, temperature=T, seed=seed, top_k=K, top_p=Pp)
+        ar = gm.session(MICRO_PROMPT, 3, 0, 0, 12, ar=True, temperature=T, seed=seed, top_k=K,
+                        top_p=Pp)
+        toks = ar.decode()
+        ar.close()
+        for i, m in enumerate(ref.margins):
+            if m < TOL:
+                break
+            assert toks[i] == ref.tokens[i], f"AR seed {seed} token {i}"
+            compared += 1
+    assert compared >= 24
+
+
+def test_micro_restricted_sampling_distribution(micro):
+    s, w, gm, om = micro
+    T, N, W, G, K, Pp = 1.5, 3, 3, 3, 4, 0.8
+    probs = exact_ar_probs(om, MICRO_PROMPT, 2, T, K, Pp)
+    n = 1500
+    cnt = collections.Counter()
+    print("micro top-K / top-P distribution over 1500 seeds", flush=True)
+    for seed in range(n):
+        win = synth.gen_window(N, W, s.vocab, seed=100 + seed)
+        ses = gm.session(MICRO_PROMPT, N, W, G, 2, window=win, prompt_ref=True,
+                         temperature=T, seed=seed, graph=False, top_k=K, top_p=Pp)
+        cnt[tuple(ses.decode())] += 1
+        ses.close()
+    assert all(probs[key] > 0 for key in cnt)      # nothing outside the cut
+    assert _gof(cnt, probs, n) > 1e-3
+
+
+def test_bf16_top1_and_vanishing_top_p_are_greedy():
+    s = synth.SHAPES["small_bf16"]
+    w = synth.gen_weights(s, 0)
+    gm = Model(s, w)
+    prompt = synth.prompt_zipf_spans(s.vocab, length=64, seed=1)
+    N, W, G, n_new = 4, 6, 6, 32
+    win = synth.gen_window(N, W, s.vocab, seed=2)
+    ar = gm.session(prompt, N, W, G, n_new, ar=True)
+    greedy = ar.decode()
+    ar.close()
+    for K, Pp in [(1, 0.0), (0, 1e-7), (1, 0.5)]:
+        print(f"small_bf16 T=1 top_k={K} top_p={Pp}", flush=True)
+        ses = gm.session(prompt, N, W, G, n_new, window=win, prompt_ref=True, temperature=1.0,
+                         seed=3, top_k=K, top_p=Pp)
+        assert ses.decode() == greedy
+        ses.close()
+        ar = gm.session(prompt, N, W, G, n_new, ar=True, temperature=1.0, seed=4, top_k=K,
+                        top_p=Pp)
+        assert ar.decode() == greedy
+        ar.close()
+    gm.close()

@@ -63,6 +63,10 @@ def test_session_bytes_and_param_validation():
     # a temperature and a seed change nothing in the workspace
     p_s = B.DecodeParams(5, 15, 15, 0, 400, 256, -1, B.LA_PROMPT_REF, 0.8, 0, 12345)
     assert B.la_session_bytes(m, p_s) == n
+    # nor do top-K / top-P (K past the vocabulary and p = 1 are no cut)
+    for k, pp in [(40, 0.9), (1, 0.0), (10 ** 6, 1.0)]:
+        p_k = B.DecodeParams(5, 15, 15, 0, 400, 256, -1, B.LA_PROMPT_REF, 0.8, k, 12345, pp)
+        assert B.la_session_bytes(m, p_k) == n
     for bad in [B.DecodeParams(1, 4, 4, 0, 100, 10, -1, 0), B.DecodeParams(17, 4, 4, 0, 100, 10, -1, 0),
                 B.DecodeParams(3, -1, 4, 0, 100, 10, -1, 0), B.DecodeParams(3, 4, 4, 0, 100, 0, -1, 0),
                 B.DecodeParams(3, 4, 4, 0, 100, 10, 4000, 0), B.DecodeParams(3, 4, 4, 0, 100, 10, -1, 64),
@@ -71,7 +75,12 @@ def test_session_bytes_and_param_validation():
                 B.DecodeParams(3, 4, 4, 0, 100, 10, -1, 0, -0.5, 0, 1),
                 B.DecodeParams(3, 4, 4, 0, 100, 10, -1, 0, float("nan"), 0, 1),
                 B.DecodeParams(3, 4, 4, 0, 100, 10, -1, 0, float("inf"), 0, 1),
-                B.DecodeParams(3, 4, 4, 0, 100, 10, -1, 0, 1.0, 7, 1)]:
+                B.DecodeParams(3, 4, 4, 0, 100, 10, -1, 0, 1.0, 0, 1, 0.0, 7),
+                # top-K / top-P out of range
+                B.DecodeParams(3, 4, 4, 0, 100, 10, -1, 0, 1.0, -1, 1),
+                B.DecodeParams(3, 4, 4, 0, 100, 10, -1, 0, 1.0, 0, 1, 1.5),
+                B.DecodeParams(3, 4, 4, 0, 100, 10, -1, 0, 1.0, 0, 1, -0.1),
+                B.DecodeParams(3, 4, 4, 0, 100, 10, -1, 0, 1.0, 0, 1, float("nan"))]:
         with pytest.raises(B.LaError) as e:
             B.la_session_bytes(m, bad)
         assert e.value.code == B.LA_EINVAL
