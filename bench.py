@@ -62,6 +62,10 @@ def parse():
     ap.add_argument("--attention", action="store_true",
                     help="instead: time the lookahead attention call alone (32 heads, head_dim 128, "
                          "bf16) at prefixes 512, 2048, 8192 for (N, W, G) = (5, 15, 15) and (7, 7, 7)")
+    ap.add_argument("--gemm", action="store_true",
+                    help="instead: time the projection GEMM call alone (split-K product and its "
+                         "piece reduction) for the shape's four projection weights at the step's "
+                         "row count and at one row, cold weights")
     ap.add_argument("--calibrate", choices=["on", "off"], nargs="?", const="on", default="on",
                     help="first run a 1 GiB HBM read (la_probe_read): the achievable read "
                          "bandwidth the fractions are also reported against, and the "
@@ -276,6 +280,56 @@ def attention_bench(read_gbps):
             torch.cuda.empty_cache()
 
 
+def gemm_bench(shape, rows, read_gbps, reps=10):
+    """The projection GEMM call alone (la_kernel_gemm: the split-K product,
+    then the in-order sum of its pieces) on seeded N(0, 0.02) bf16 weights of
+    the shape's QKV, O, gate/up and down matrices, at `rows` rows and at one
+    row.  Three weight sets rotate so every call streams cold weights.
+    Bytes per call = weights + x + the float32 output."""
+    import torch
+    from exact_decoding_amd import binding as B
+    d, F = shape.d_model, shape.d_ff
+    nqkv = (shape.n_heads + 2 * shape.n_kv_heads) * shape.head_dim
+    mats = (("QKV", nqkv, d), ("O", d, shape.n_heads * shape.head_dim), ("gate/up", 2 * F, d),
+            ("down", d, F))
+    g = torch.Generator(device="cuda").manual_seed(11)
+    nset = 3
+    for name, N, K in mats:
+        sets = []
+        for _ in range(nset):
+            w = (torch.randn(N, K, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+            dst = torch.empty(B.la_packed_bytes(N, K), dtype=torch.uint8, device="cuda")
+            B.la_pack_weight(w, N, K, dst, None)
+            del w
+            sets.append(dst)
+        torch.cuda.synchronize()
+        for M in (rows, 1):
+            x = torch.randn(M, K, device="cuda", generator=g).to(torch.bfloat16)
+            y = torch.empty(M, N, dtype=torch.float32, device="cuda")
+            ws = torch.empty(max(B.la_kernel_gemm_ws_bytes(M, K, N), 4), dtype=torch.uint8,
+                             device="cuda")
+            for i in range(nset):
+                B.la_kernel_gemm(x, M, K, sets[i % nset], N, y, B.LA_BF16, ws, None)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(reps * nset):
+                B.la_kernel_gemm(x, M, K, sets[i % nset], N, y, B.LA_BF16, ws, None)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / (reps * nset) * 1e3
+            nbytes = N * K * 2 + M * K * 2 + M * N * 4
+            gbps = nbytes / (us * 1e-6) / 1e9
+            print(json.dumps({"kernel": "projection GEMM call (product + piece sum)",
+                              "matrix": name, "N": N, "K": K, "rows": M, "us_per_call": us,
+                              "bytes_per_call": nbytes, "GBps": gbps, "frac": gbps / HBM_PEAK_GBPS,
+                              "frac_of_achievable": gbps / read_gbps if read_gbps else None}),
+                  flush=True)
+            del x, y, ws
+        del sets
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -295,6 +349,9 @@ def main():
         log(f"[bench] calibration: 1 GiB read at {read_gbps:.0f} GB/s")
     if args.attention:
         attention_bench(read_gbps)
+        return
+    if args.gemm:
+        gemm_bench(shape, 1 + (W + G) * (N - 1), read_gbps)
         return
     t0 = time.time()
     log(f"[bench] generating + uploading {shape.name} weights")
