@@ -43,6 +43,15 @@ R10 Budget: the emitted tokens of the last step are truncated to max_new;
 R11 Prompt as reference: every prompt n-gram prompt[j .. j+N-1],
     j = 0 .. n-N, is inserted in increasing j before the first step.
 R12 Only lookahead harvests and the prompt feed the pool.
+R21 Pool eviction by recency (the pages leave the pool's size cap and its
+    eviction policy unablated and name LRU and FIFO as the policies to
+    compare, [LD] "What is not ablated" and "Memory-efficient n-gram pool
+    management"): an n-gram is "used" when it is generated again (a
+    duplicate insert from the lookahead branch or the prompt); it then
+    becomes the bucket's most recent entry, and a full bucket evicts its
+    least recent entry. Acceptance by verification is not counted as a use.
+    FIFO (R5, the default) leaves a duplicate where it is. Selection (R6)
+    takes the newest G in the bucket's order under either policy.
 R18 Sampling verification (Algorithm 4, [LD] §3.4 "Sampling verification"):
     at position i the row predicting P+i (row 0, then the row of the
     accepted prefix) gives weights e_v = exp((l_v - max l) / T); the
@@ -132,10 +141,12 @@ def block_mask(N: int, W: int, G: int) -> np.ndarray:
 
 class NGramPool:
     """Key = first token of the n-gram, value = list of suffixes ([LD] §3.4
-    "N-gram pool update"), FIFO with capacity `cap` per key (R5)."""
+    "N-gram pool update"), capacity `cap` per key, oldest first: FIFO (R5)
+    or, with lru, ordered by the last time each suffix was generated (R21)."""
 
-    def __init__(self, cap: int):
+    def __init__(self, cap: int, lru: bool = False):
         self.cap = cap
+        self.lru = lru
         self.buckets: dict[int, list[tuple[int, ...]]] = {}
         self.inserts = 0
         self.dup_skips = 0
@@ -146,6 +157,9 @@ class NGramPool:
         b = self.buckets.setdefault(int(key), [])
         if suffix in b:
             self.dup_skips += 1
+            if self.lru:                                     # R21
+                b.remove(suffix)
+                b.append(suffix)
             return
         self.inserts += 1
         if len(b) == self.cap:
@@ -378,7 +392,8 @@ def lookahead(model: OracleModel, prompt, N: int, W: int, G: int, max_new: int,
               init_window, prompt_ref: bool = False, pool_cap: int | None = None,
               eos_id: int = -1, keep_logits: bool = False,
               pool: NGramPool | None = None, temperature: float = 0.0,
-              seed: int = 0, top_k: int = 0, top_p: float = 1.0) -> DecodeResult:
+              seed: int = 0, top_k: int = 0, top_p: float = 1.0,
+              pool_lru: bool = False) -> DecodeResult:
     """Lookahead decoding, one step per loop iteration ([LD] §3.2, §3.4).
 
     Each step: select candidates for cur from the pool; run one forward
@@ -393,7 +408,7 @@ def lookahead(model: OracleModel, prompt, N: int, W: int, G: int, max_new: int,
     cache, cur = prefill(model, prompt)
     P = cache[0][0].shape[0]
     if pool is None:
-        pool = NGramPool(pool_cap if pool_cap is not None else max(G, 1))
+        pool = NGramPool(pool_cap if pool_cap is not None else max(G, 1), lru=pool_lru)
     if prompt_ref:                                           # R11
         for j in range(len(prompt) - N + 1):
             pool.insert(prompt[j], prompt[j + 1:j + N])

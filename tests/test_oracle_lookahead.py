@@ -235,6 +235,73 @@ def test_pool_fifo_and_select():
     assert p.select(8, 2) == []
 
 
+def test_pool_lru_by_hand():
+    """R21 worked by hand, cap 2: a, b, a again, c.  FIFO keeps [a, b] at the
+    repeat and evicts a for c; recency moves a behind b and evicts b."""
+    seq = [(1, 1), (2, 2), (1, 1), (3, 3)]
+    fifo, lru = la.NGramPool(2), la.NGramPool(2, lru=True)
+    for sfx in seq:
+        fifo.insert(5, sfx)
+        lru.insert(5, sfx)
+    assert fifo.buckets[5] == [(2, 2), (3, 3)]
+    assert lru.buckets[5] == [(1, 1), (3, 3)]
+    for p in (fifo, lru):
+        assert (p.inserts, p.dup_skips, p.evictions) == (3, 1, 1)
+    # selection is the newest G in the bucket's order under both policies
+    assert lru.select(5, 1) == [(3, 3)]
+    lru.insert(5, (1, 1))                 # a again: now the most recent
+    assert lru.buckets[5] == [(3, 3), (1, 1)] and lru.select(5, 1) == [(1, 1)]
+
+
+def test_pool_lru_cap_one_and_no_repeat_equal_fifo():
+    """Recency only reorders on a repeat, and a one-entry bucket has no order:
+    with cap 1, or with no repeated suffix, both policies hold the same pool."""
+    rng = np.random.default_rng(3)
+    for cap, vocab in ((1, 3), (3, 1000)):
+        fifo, lru = la.NGramPool(cap), la.NGramPool(cap, lru=True)
+        for _ in range(400):
+            key, sfx = int(rng.integers(4)), tuple(int(v) for v in rng.integers(vocab, size=2))
+            fifo.insert(key, sfx)
+            lru.insert(key, sfx)
+        assert fifo.buckets == lru.buckets
+        assert (fifo.inserts, fifo.dup_skips, fifo.evictions) == \
+            (lru.inserts, lru.dup_skips, lru.evictions)
+
+
+def test_pool_lru_is_recency_order():
+    """Against a brute-force definition: after any insert sequence, an LRU
+    bucket is the distinct suffixes ordered by their last appearance, the
+    oldest dropped to the capacity, provided no suffix was ever evicted."""
+    rng = np.random.default_rng(4)
+    for trial in range(50):
+        cap = int(rng.integers(2, 6))
+        seq = [tuple(int(v) for v in rng.integers(cap, size=1)) for _ in range(30)]
+        p = la.NGramPool(cap, lru=True)
+        for sfx in seq:
+            p.insert(0, sfx)
+        last = {sfx: i for i, sfx in enumerate(seq)}
+        assert p.buckets[0] == sorted(last, key=last.get)
+        assert p.evictions == 0
+
+
+@pytest.mark.parametrize("N,W,G,cap", [(3, 4, 4, None), (4, 5, 3, 2), (5, 3, 3, 1)])
+def test_lookahead_lru_pool_is_exact(N, W, G, cap):
+    """The pool's policy only changes which guesses are verified, never the
+    output: lookahead with the recency pool equals greedy AR."""
+    s = synth.SHAPES["micro"]
+    om = OracleModel(s, synth.gen_weights(s, 0))
+    prompt = np.array([1, 2, 3, 4, 1, 2, 3, 4, 5, 6, 7, 1, 2, 3], dtype=np.int64) % s.vocab
+    win = synth.gen_window(N, W, s.vocab, seed=2)
+    ref = la.greedy_ar(om, prompt, 40).tokens
+    r = la.lookahead(om, prompt, N, W, G, 40, win, prompt_ref=True, pool_cap=cap, pool_lru=True)
+    assert r.tokens == ref
+    assert r.pool.lru and all(len(b) <= r.pool.cap for b in r.pool.buckets.values())
+    if (N, W, G) == (3, 4, 4):
+        # this run repeats suffixes in full buckets: the two policies diverge
+        f = la.lookahead(om, prompt, N, W, G, 40, win, prompt_ref=True, pool_cap=cap)
+        assert (f.pool.inserts, f.pool.evictions) != (r.pool.inserts, r.pool.evictions)
+
+
 def test_slide():
     win = np.arange(12).reshape(3, 4)
     new = np.array([90, 91, 92, 93])
