@@ -55,6 +55,10 @@ def parse():
     ap.add_argument("--seed", type=int, default=0, help="key of the sampling draws")
     ap.add_argument("--top-k", type=int, default=0, help="sampling: top-K cut (0 = none)")
     ap.add_argument("--top-p", type=float, default=0.0, help="sampling: top-P cut (0 = none)")
+    ap.add_argument("--pool-lru", action="store_true",
+                    help="evict pool n-grams by recency instead of FIFO (LA_POOL_LRU)")
+    ap.add_argument("--pool-cap", type=int, default=0,
+                    help="suffixes kept per first token (0 = G)")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the benchmark line: step time against the row count "
                          "M over a grid of (N, W = G), one JSON line per configuration")
@@ -381,7 +385,8 @@ def main():
     def la_session():
         return model.session(prompt, N, W, G, args.max_new, window=window, prompt_ref=True,
                              graph=graph, temperature=args.temperature, seed=args.seed,
-                             top_k=args.top_k, top_p=args.top_p)
+                             top_k=args.top_k, top_p=args.top_p, pool_cap=args.pool_cap,
+                             pool_lru=args.pool_lru)
 
     def ar_session():
         return model.session(prompt, N, W, G, args.max_new, ar=True, graph=graph,
@@ -396,7 +401,11 @@ def main():
             break
         ses.step()
     ses.decode()
-    gen_steps = ses.stats()["steps"]
+    gen_stats = ses.stats()
+    gen_steps = gen_stats["steps"]
+    pool_stats = {k: gen_stats[k] for k in ("inserts", "dup_skips", "evictions", "pool_ngrams",
+                                             "pool_keys_nonempty", "gathers_nonempty", "cand_total")
+                  if k in gen_stats}
     la_tokens_ref = list(ses.tokens)
     ses.close()
     S = args.max_new / gen_steps
@@ -512,7 +521,9 @@ def main():
                                f"{args.max_new} new tokens per generation",
                    "N": N, "W": W, "G": G, "rows_per_step": M, "parallelism": "single GPU",
                    "graph": graph, "temperature": args.temperature, "top_k": args.top_k,
-                   "top_p": args.top_p},
+                   "top_p": args.top_p, "pool": "lru" if args.pool_lru else "fifo",
+                   "pool_cap": args.pool_cap or G},
+        "pool_one_generation": pool_stats,
         "step_compression": S,
         "step_compression_prompt_seeds": S_seeds,
         "prefill_ms": prefill_ms,

@@ -41,7 +41,12 @@ struct InsertCounts {
   int ins, dup, ev, ngr, keys;
 };
 
-// Insert (key, sfx[0..n1)) into the pool; one thread.
+// Insert (key, sfx[0..n1)) into the pool; one thread.  A bucket is a ring
+// of cap entries, oldest at head.  A suffix already present is counted as a
+// repeat and, with lru, moved to the newest end (the entries after it move
+// one place towards the head), so that eviction drops the suffix generated
+// least recently ([LD] "Memory-efficient n-gram pool management" names LRU
+// and FIFO as the policies to compare; FIFO leaves it in place).
 __device__ void pool_insert(const PoolDesc& p, int key, const int32_t* sfx, InsertCounts& c) {
   const int cnt = p.cnt[key];
   const int head = p.head[key];
@@ -51,7 +56,25 @@ __device__ void pool_insert(const PoolDesc& p, int key, const int32_t* sfx, Inse
     const int32_t* b = bucket(p, key, idx);
     bool same = true;
     for (int i = 0; i < p.n1; ++i) same = same && (b[i] == sfx[i]);
-    if (same) { ++c.dup; return; }
+    if (same) {
+      ++c.dup;
+      if (p.lru) {
+        for (int f = e; f + 1 < cnt; ++f) {
+          int from = head + f + 1;
+          if (from >= p.cap) from -= p.cap;
+          int to = head + f;
+          if (to >= p.cap) to -= p.cap;
+          int32_t* dst = bucket(p, key, to);
+          const int32_t* src = bucket(p, key, from);
+          for (int i = 0; i < p.n1; ++i) dst[i] = src[i];
+        }
+        int last = head + cnt - 1;
+        if (last >= p.cap) last -= p.cap;
+        int32_t* dst = bucket(p, key, last);
+        for (int i = 0; i < p.n1; ++i) dst[i] = sfx[i];
+      }
+      return;
+    }
   }
   ++c.ins;
   int idx;

@@ -81,7 +81,7 @@ struct Views {
 struct Shape {
   int L, d, H, Hkv, hd, F, V, dt;
   int M, rows_cap, ld_ctx;
-  int N, W, G, cap;
+  int N, W, G, cap, lru;
   SplitPlan sp_qkv, sp_o, sp_gu, sp_d, sp_lm;
   double pc_qkv, pc_o, pc_gu, pc_d;  // mean pieces per column block (profile bytes)
   int att_mfma, att_nsplit;  // MFMA-attention prefix chunks (0 = per-row kernel only)
@@ -97,6 +97,7 @@ Shape make_shape(const la_model* m, const la_decode_params* p) {
   s.W = ar ? 0 : p->W;
   s.G = ar ? 0 : p->G;
   s.cap = p->pool_cap > 0 ? p->pool_cap : (s.G > 0 ? s.G : 1);
+  s.lru = (p->flags & LA_POOL_LRU) != 0;
   s.M = 1 + (s.W + s.G) * (s.N - 1);
   s.ld_ctx = p->max_ctx;
   s.rows_cap = s.M > p->max_ctx ? s.M : p->max_ctx;
@@ -175,7 +176,7 @@ int check_params(const la_model* m, const la_decode_params* p) {
   if (p->max_ctx < 2) return fail(LA_EINVAL, "max_ctx must be >= 2");
   if (p->max_new < 1) return fail(LA_EINVAL, "max_new must be >= 1");
   if (p->eos_id >= m->d.vocab) return fail(LA_EINVAL, "eos_id out of range");
-  if (p->flags & ~(LA_PROMPT_REF | LA_AR | LA_NO_GRAPH)) return fail(LA_EINVAL, "unknown flags");
+  if (p->flags & ~(LA_PROMPT_REF | LA_AR | LA_NO_GRAPH | LA_POOL_LRU)) return fail(LA_EINVAL, "unknown flags");
   const long long W = ar ? 0 : p->W, G = ar ? 0 : p->G;
   const long long M = 1 + (W + G) * (p->N - 1);
   if (M > 2048) return fail(LA_EINVAL, "1 + (W+G)(N-1) must be <= 2048");
@@ -405,7 +406,7 @@ int enqueue_step(la_session* ss) {
   hipStream_t st = ss->stream;
   const int dt = s.dt;
   PoolDesc pool{ss->at<int32_t>(ss->v.pool_tok), ss->at<int32_t>(ss->v.pool_cnt),
-                ss->at<int32_t>(ss->v.pool_head), s.V, s.cap, s.N - 1};
+                ss->at<int32_t>(ss->v.pool_head), s.V, s.cap, s.N - 1, s.lru};
   StepIO io{};
   io.st = ss->at<DevState>(ss->v.st);
   io.win = ss->at<int32_t>(ss->v.win);
@@ -630,7 +631,7 @@ int la_prefill(la_model* m, const la_decode_params* p, const int32_t* prompt, in
   }
   if ((p->flags & LA_PROMPT_REF) && s.G > 0 && n_prompt >= s.N) {
     PoolDesc pool{ss->at<int32_t>(v.pool_tok), ss->at<int32_t>(v.pool_cnt),
-                  ss->at<int32_t>(v.pool_head), s.V, s.cap, n1};
+                  ss->at<int32_t>(v.pool_head), s.V, s.cap, n1, s.lru};
     LA_PF(launch_pool_seed(pool, ss->at<DevState>(v.st), ss->at<int32_t>(v.prompt), n_prompt, st));
   }
   LA_PF(hipStreamSynchronize(st));

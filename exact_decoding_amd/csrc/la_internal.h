@@ -190,6 +190,7 @@ struct PoolDesc {
   int32_t* cnt;   // [V]
   int32_t* head;  // [V]
   int V, cap, n1; // n1 = N - 1
+  int lru;        // 1: a repeated suffix becomes the bucket's newest entry
 };
 struct StepIO {
   DevState* st;

@@ -61,7 +61,7 @@ typedef struct {
  * W  window width (columns), >= 0.
  * G  max verification candidates per step, >= 0 ([LD] §3.4 "N-gram
  *    selection from the pool").
- * pool_cap   suffixes kept per first token (FIFO); 0 means G (min 1).
+ * pool_cap   suffixes kept per first token; 0 means G (min 1).
  * max_ctx    KV-cache capacity in positions.
  * max_new    tokens to generate.
  * eos_id     stop after emitting this id; -1 for none.
@@ -71,6 +71,15 @@ typedef struct {
  *              kernels (W = G = 0 internally; one token per step).
  *            LA_NO_GRAPH: launch every step's kernels eagerly instead of
  *              replaying a captured HIP graph.
+ *            LA_POOL_LRU: evict by recency instead of FIFO.  A suffix that
+ *              is generated again (from the window or the prompt) becomes
+ *              its bucket's newest entry, so a full bucket drops the one
+ *              generated least recently.  The pages leave the pool's cap and
+ *              eviction policy unablated and name LRU and FIFO as the
+ *              policies to compare ([LD] "What is not ablated",
+ *              "Memory-efficient n-gram pool management").  Selection (the
+ *              newest G of the bucket) and the output tokens are unchanged;
+ *              repeats are still counted in dup_skips.
  * temperature  0: greedy verification ([LD] §3.4 "Greedy verification
  *              algorithm (Algorithm 3)").  > 0: sampling verification
  *              ([LD] §3.4 "Sampling verification (Algorithm 4)") against
@@ -102,6 +111,7 @@ typedef struct {
 #define LA_PROMPT_REF 1u
 #define LA_AR 2u
 #define LA_NO_GRAPH 8u
+#define LA_POOL_LRU 16u
 
 /* Statistics since prefill ([LD] §3.4 "Scaling Law": S = tokens / steps). */
 typedef struct {

@@ -230,3 +230,50 @@ def test_vocab_not_multiple_of_four_matches_oracle():
     assert ses.decode() == ar.tokens
     ses.close()
     gm.close()
+
+
+@pytest.fixture(scope="module")
+def micro():
+    s = synth.SHAPES["micro"]
+    w = synth.gen_weights(s, 0)
+    return s, w, Model(s, w), OracleModel(s, w)
+
+
+MICRO_PROMPT = [1, 2, 3, 4, 1, 2, 3, 4, 5, 6, 7, 1, 2, 3]
+
+
+@pytest.mark.parametrize("N,W,G,cap,graph", [(3, 4, 4, 0, True), (3, 4, 4, 0, False),
+                                             (4, 5, 3, 2, True), (5, 3, 3, 1, True)])
+def test_micro_lru_pool_matches_oracle(micro, N, W, G, cap, graph):
+    """Recency eviction (LA_POOL_LRU): on the 8-token fp32 model, whose
+    greedy decisions all have top-2 margins above 1e-2 in every block row,
+    the GPU emits the greedy AR tokens in the oracle's steps, with the
+    oracle's accepted-length histogram and pool counters under the same
+    policy.  At (3, 4, 4) the two policies' counters differ on the GPU as
+    they do in the oracle, so the recency path is exercised."""
+    s, w, gm, om = micro
+    n_new = 40
+    prompt = np.array(MICRO_PROMPT, dtype=np.int64) % s.vocab
+    win = synth.gen_window(N, W, s.vocab, seed=2)
+    print(f"micro lru N={N} W={W} G={G} cap={cap} graph={graph}", flush=True)
+    ar = la.greedy_ar(om, prompt, n_new)
+    stats = {}
+    for lru in (True, False):
+        ref = la.lookahead(om, prompt, N, W, G, n_new, win, prompt_ref=True,
+                           pool_cap=cap or None, pool_lru=lru)
+        assert ref.tokens == ar.tokens
+        ses = gm.session(prompt, N, W, G, n_new, window=win, prompt_ref=True, graph=graph,
+                         pool_cap=cap, pool_lru=lru)
+        toks = ses.decode()
+        st = ses.stats()
+        ses.close()
+        assert toks == ar.tokens
+        assert st["steps"] == ref.steps
+        assert [st["accept_hist"][j] for j in range(N)] == [ref.accepted.count(j) for j in range(N)]
+        got = (st["inserts"], st["dup_skips"], st["evictions"], st["pool_ngrams"],
+               st["pool_keys_nonempty"])
+        assert got == (ref.pool.inserts, ref.pool.dup_skips, ref.pool.evictions,
+                       ref.pool.n_ngrams(), ref.pool.n_keys()), (lru, got)
+        stats[lru] = got
+    if (N, W, G) == (3, 4, 4):
+        assert stats[True] != stats[False]
