@@ -334,7 +334,7 @@ __global__ __launch_bounds__(64) void k_attn_tail(AttnDesc a) {
 // MFMA part (bf16, head_dim 128): one workgroup per (head, prefix chunk
 // committed positions, block of 128 rows).  Each 64-position tile of K and V
 // is staged in LDS once and used by every row; wave w handles the 16-row
-// groups w and w+4, both on each tile (group_tile2).
+// groups w and w+4, both on each tile (group_tiles<2>).
 //
 // Scores are computed transposed, S^T = K Q^T (v_mfma_f32_16x16x32_bf16,
 // A = 16 keys x 32 dims of K, B = 32 dims x 16 rows of Q^T), so a lane holds
@@ -369,120 +369,51 @@ __device__ __forceinline__ void group_load(const AttnDesc& a, int h, int Pc, int
   }
 }
 
-// One group's online-softmax update from the 64-key tile [t0, t0 + 64)
-// staged in Ks / Vt; keys at or past a row's F are masked.
-__device__ __forceinline__ void group_tile(const bf16_t* Ks, const bf16_t* Vt, int t0, int F,
-                                           const U4 (&qf)[4], f32x4_t (&o)[8], float& m_run,
-                                           float& l_run, int c16, int q4, float scale) {
-  // no fused multiply-adds: group_tile2 then rounds every step as this does
-#pragma clang fp contract(off)
-  // keys [t0, F) of the tile are this lane's row's (F a multiple of BT)
-  const int nv = F - t0;
-  // skip the group when the tile is past every one of its rows
-  if (!__any(nv > 0)) return;
-  f32x4_t st[4];
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    st[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      U4 ka;
-      ka.u = *(const u32x4_t*)(&Ks[(kb * 16 + c16) * KSTR + ks * 32 + q4 * 8]);
-      st[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka.v, qf[ks].v, st[kb], 0, 0, 0);
-    }
-  }
-  float mt = -INFINITY;
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float sv = kb * 16 + 4 * q4 + e < nv ? st[kb][e] * scale : -INFINITY;
-      st[kb][e] = sv;
-      mt = fmaxf(mt, sv);
-    }
-  mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-  mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-  const float m_new = fmaxf(m_run, mt);
-  const float alpha = m_new == -INFINITY ? 1.0f : exp_e(m_run - m_new);
-  // p enters the PV product as the sum of two bf16 values, hi = bf16(p)
-  // and lo = bf16(p - hi) (p - hi is exact in fp32), so the product
-  // carries p to about 2^-17 relative, as an fp32 product would: no
-  // rounding of the probabilities beyond the fp32 arithmetic
-  float ls = 0.f;
-  U4 pa[2], pl[2];
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float pv = kb * 16 + 4 * q4 + e < nv ? exp_e(st[kb][e] - m_new) : 0.f;
-      ls += pv;
-      const uint16_t hb = bf16_rne(pv);
-      pa[kb >> 1].h[(kb & 1) * 4 + e] = hb;
-      pl[kb >> 1].h[(kb & 1) * 4 + e] = bf16_rne(pv - __uint_as_float((uint32_t)hb << 16));
-    }
-  ls += __shfl_xor(ls, 16, 64);
-  ls += __shfl_xor(ls, 32, 64);
-  l_run = l_run * alpha + ls;
-  m_run = m_new;
-  // rescale O rows 4*q4 + e by their row's alpha (held by lane 4*q4 + e)
-  float al[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) al[e] = __shfl(alpha, q4 * 4 + e, 64);
-#pragma unroll
-  for (int db = 0; db < 8; ++db)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) o[db][e] *= al[e];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-#pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      const bf16_t* vr = &Vt[(db * 16 + c16) * VSTR + 32 * j + 4 * q4];
-      U4 vb;
-      const u32x2_t lo = *(const u32x2_t*)vr;
-      const u32x2_t hi = *(const u32x2_t*)(vr + 16);
-      vb.u = u32x4_t{lo.x, lo.y, hi.x, hi.y};
-      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[j].v, vb.v, o[db], 0, 0, 0);
-      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl[j].v, vb.v, o[db], 0, 0, 0);
-    }
-  }
-}
-
-// Both 16-row groups of a wave on one tile, step by step: the K fragment
-// of each MFMA and the V^T fragment of each P.V step are read from LDS once
-// for the two groups, and the two groups' chains (scores -> row max ->
-// probabilities -> P.V) interleave, so one group's shuffle and exponential
-// latencies overlap the other's.  Each group's arithmetic is exactly
-// group_tile's: a group whose rows all end before the tile takes alpha = 1
-// and p = 0 for every row, which leaves its state bit for bit unchanged, as
-// group_tile's early return does.
-__device__ __forceinline__ void group_tile2(const bf16_t* Ks, const bf16_t* Vt, int t0,
+// The online-softmax update of NG 16-row groups of one wave from the 64-key
+// tile [t0, t0 + 64) staged in Ks / Vt; keys at or past a row's F are
+// masked.  With NG = 2 the steps of the two groups interleave (the K
+// fragment of each MFMA and the V^T fragment of each P.V step are read from
+// LDS once for both, and one group's shuffle and exponential latencies
+// overlap the other's); each group's arithmetic is the same for NG = 1 and
+// NG = 2, which a verification row (two groups per wave at 121 rows) and the
+// autoregressive query at its position (one group) rely on for bit-identical
+// outputs.  No fused multiply-adds: otherwise the compiler fuses the score
+// scaling into the exponent's subtraction in one instance and not the other.
+// A group whose rows all end before the tile takes alpha = 1 and p = 0 for
+// every row, which leaves its state bit for bit unchanged.
+template <int NG>
+__device__ __forceinline__ void group_tiles(const bf16_t* Ks, const bf16_t* Vt, int t0,
                                             const int (&F)[2], const U4 (&qf)[2][4],
                                             f32x4_t (&o)[2][8], float (&m_run)[2],
                                             float (&l_run)[2], int c16, int q4, float scale) {
-  // no fused multiply-adds, as in group_tile: the compiler would otherwise
-  // fuse the score scaling into the exponent's subtraction here and not there
 #pragma clang fp contract(off)
-  int nv[2];
+  // keys [t0, F) of the tile are this lane's row's (F a multiple of BT)
+  int nv[NG];
+  bool any = false;
 #pragma unroll
-  for (int gi = 0; gi < 2; ++gi) nv[gi] = F[gi] - t0;
-  if (!__any(nv[0] > 0 || nv[1] > 0)) return;
-  f32x4_t st[2][4];
+  for (int gi = 0; gi < NG; ++gi) {
+    nv[gi] = F[gi] - t0;
+    any = any || nv[gi] > 0;
+  }
+  // skip the tile when it is past every row of the groups
+  if (!__any(any)) return;
+  f32x4_t st[NG][4];
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
-    for (int gi = 0; gi < 2; ++gi) st[gi][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int gi = 0; gi < NG; ++gi) st[gi][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       U4 ka;
       ka.u = *(const u32x4_t*)(&Ks[(kb * 16 + c16) * KSTR + ks * 32 + q4 * 8]);
 #pragma unroll
-      for (int gi = 0; gi < 2; ++gi)
+      for (int gi = 0; gi < NG; ++gi)
         st[gi][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka.v, qf[gi][ks].v, st[gi][kb], 0, 0, 0);
     }
   }
-  float mt[2];
+  float mt[NG];
 #pragma unroll
-  for (int gi = 0; gi < 2; ++gi) {
+  for (int gi = 0; gi < NG; ++gi) {
     mt[gi] = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
@@ -494,16 +425,19 @@ __device__ __forceinline__ void group_tile2(const bf16_t* Ks, const bf16_t* Vt, 
       }
   }
 #pragma unroll
-  for (int gi = 0; gi < 2; ++gi) mt[gi] = fmaxf(mt[gi], __shfl_xor(mt[gi], 16, 64));
+  for (int gi = 0; gi < NG; ++gi) mt[gi] = fmaxf(mt[gi], __shfl_xor(mt[gi], 16, 64));
 #pragma unroll
-  for (int gi = 0; gi < 2; ++gi) mt[gi] = fmaxf(mt[gi], __shfl_xor(mt[gi], 32, 64));
-  float alpha[2], m_new[2], ls[2];
-  U4 pa[2][2], pl[2][2];
+  for (int gi = 0; gi < NG; ++gi) mt[gi] = fmaxf(mt[gi], __shfl_xor(mt[gi], 32, 64));
+  // p enters the PV product as the sum of two bf16 values, hi = bf16(p)
+  // and lo = bf16(p - hi) (p - hi is exact in fp32), so the product
+  // carries p to about 2^-17 relative, as an fp32 product would: no
+  // rounding of the probabilities beyond the fp32 arithmetic
+  float alpha[NG], m_new[NG], ls[NG];
+  U4 pa[NG][2], pl[NG][2];
 #pragma unroll
-  for (int gi = 0; gi < 2; ++gi) {
+  for (int gi = 0; gi < NG; ++gi) {
     m_new[gi] = fmaxf(m_run[gi], mt[gi]);
     alpha[gi] = m_new[gi] == -INFINITY ? 1.0f : exp_e(m_run[gi] - m_new[gi]);
-    // p as hi + lo bf16 parts, as in group_tile
     ls[gi] = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
@@ -517,19 +451,20 @@ __device__ __forceinline__ void group_tile2(const bf16_t* Ks, const bf16_t* Vt, 
       }
   }
 #pragma unroll
-  for (int gi = 0; gi < 2; ++gi) ls[gi] += __shfl_xor(ls[gi], 16, 64);
+  for (int gi = 0; gi < NG; ++gi) ls[gi] += __shfl_xor(ls[gi], 16, 64);
 #pragma unroll
-  for (int gi = 0; gi < 2; ++gi) ls[gi] += __shfl_xor(ls[gi], 32, 64);
-  float al[2][4];
+  for (int gi = 0; gi < NG; ++gi) ls[gi] += __shfl_xor(ls[gi], 32, 64);
+  // rescale O rows 4*q4 + e by their row's alpha (held by lane 4*q4 + e)
+  float al[NG][4];
 #pragma unroll
-  for (int gi = 0; gi < 2; ++gi) {
+  for (int gi = 0; gi < NG; ++gi) {
     l_run[gi] = l_run[gi] * alpha[gi] + ls[gi];
     m_run[gi] = m_new[gi];
 #pragma unroll
     for (int e = 0; e < 4; ++e) al[gi][e] = __shfl(alpha[gi], q4 * 4 + e, 64);
   }
 #pragma unroll
-  for (int gi = 0; gi < 2; ++gi)
+  for (int gi = 0; gi < NG; ++gi)
 #pragma unroll
     for (int db = 0; db < 8; ++db)
 #pragma unroll
@@ -544,7 +479,7 @@ __device__ __forceinline__ void group_tile2(const bf16_t* Ks, const bf16_t* Vt, 
       const u32x2_t hi = *(const u32x2_t*)(vr + 16);
       vb.u = u32x4_t{lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
-      for (int gi = 0; gi < 2; ++gi) {
+      for (int gi = 0; gi < NG; ++gi) {
         o[gi][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[gi][j].v, vb.v, o[gi][db], 0, 0, 0);
         o[gi][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl[gi][j].v, vb.v, o[gi][db], 0, 0, 0);
       }
@@ -665,9 +600,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __syncthreads();
     if (t0 + AT < tend) fetch(t0 + AT);
     if (gon[1])
-      group_tile2(Ks, Vt, t0, F, qf, o, m_run, l_run, c16, q4, scale);
+      group_tiles<2>(Ks, Vt, t0, F, qf, o, m_run, l_run, c16, q4, scale);
     else if (gon[0])
-      group_tile(Ks, Vt, t0, F[0], qf[0], o[0], m_run[0], l_run[0], c16, q4, scale);
+      group_tiles<1>(Ks, Vt, t0, F, qf, o, m_run, l_run, c16, q4, scale);
     __syncthreads();
   }
 #pragma unroll
