@@ -52,6 +52,17 @@ R21 Pool eviction by recency (the pages leave the pool's size cap and its
     least recent entry. Acceptance by verification is not counted as a use.
     FIFO (R5, the default) leaves a duplicate where it is. Selection (R6)
     takes the newest G in the bucket's order under either policy.
+R22 Selection by a longer match (the pages contrast matching only the first
+    token with matching longer prefixes, and note that the prompt-lookup
+    baseline checks several starting tokens, [LD] Table 3 and "What is not
+    ablated"): every entry also keeps its context, the token just before the
+    n-gram's first token where it was generated (a window column's context
+    is the level-0 token of the column to its left, or the step's current
+    token for the first column; a prompt n-gram's is the prompt token before
+    it, none for the first). A repeat takes the new context. With selection
+    by context, the G taken are the newest entries whose context equals the
+    token before cur, then the newest of the rest; they are presented in the
+    bucket's order, oldest first, as in R6.
 R18 Sampling verification (Algorithm 4, [LD] §3.4 "Sampling verification"):
     at position i the row predicting P+i (row 0, then the row of the
     accepted prefix) gives weights e_v = exp((l_v - max l) / T); the
@@ -148,29 +159,42 @@ class NGramPool:
         self.cap = cap
         self.lru = lru
         self.buckets: dict[int, list[tuple[int, ...]]] = {}
+        self.context: dict[tuple[int, tuple[int, ...]], int] = {}   # R22
         self.inserts = 0
         self.dup_skips = 0
         self.evictions = 0
 
-    def insert(self, key: int, suffix) -> None:
+    def insert(self, key: int, suffix, context: int = -1) -> None:
+        key = int(key)
         suffix = tuple(int(t) for t in suffix)
-        b = self.buckets.setdefault(int(key), [])
+        b = self.buckets.setdefault(key, [])
         if suffix in b:
             self.dup_skips += 1
             if self.lru:                                     # R21
                 b.remove(suffix)
                 b.append(suffix)
+            self.context[(key, suffix)] = int(context)       # R22
             return
         self.inserts += 1
         if len(b) == self.cap:
-            b.pop(0)
+            del self.context[(key, b.pop(0))]
             self.evictions += 1
         b.append(suffix)
+        self.context[(key, suffix)] = int(context)
 
-    def select(self, key: int, G: int) -> list[tuple[int, ...]]:
-        """Up to G suffixes whose n-gram starts with `key` (R6)."""
+    def select(self, key: int, G: int, prev: int | None = None) -> list[tuple[int, ...]]:
+        """Up to G suffixes whose n-gram starts with `key`: the newest (R6),
+        or, given the token `prev` before key, the newest whose context is
+        prev and then the newest of the rest (R22); oldest first."""
         b = self.buckets.get(int(key), [])
-        return list(b[-G:]) if G > 0 else []
+        if G <= 0:
+            return []
+        if prev is None:
+            return list(b[-G:])
+        newest_first = list(range(len(b) - 1, -1, -1))
+        match = [i for i in newest_first if self.context[(int(key), b[i])] == prev]
+        rest = [i for i in newest_first if self.context[(int(key), b[i])] != prev]
+        return [b[i] for i in sorted((match + rest)[:G])]
 
     def n_ngrams(self) -> int:
         return sum(len(b) for b in self.buckets.values())
@@ -393,7 +417,7 @@ def lookahead(model: OracleModel, prompt, N: int, W: int, G: int, max_new: int,
               eos_id: int = -1, keep_logits: bool = False,
               pool: NGramPool | None = None, temperature: float = 0.0,
               seed: int = 0, top_k: int = 0, top_p: float = 1.0,
-              pool_lru: bool = False) -> DecodeResult:
+              pool_lru: bool = False, pool_context: bool = False) -> DecodeResult:
     """Lookahead decoding, one step per loop iteration ([LD] §3.2, §3.4).
 
     Each step: select candidates for cur from the pool; run one forward
@@ -411,7 +435,8 @@ def lookahead(model: OracleModel, prompt, N: int, W: int, G: int, max_new: int,
         pool = NGramPool(pool_cap if pool_cap is not None else max(G, 1), lru=pool_lru)
     if prompt_ref:                                           # R11
         for j in range(len(prompt) - N + 1):
-            pool.insert(prompt[j], prompt[j + 1:j + N])
+            pool.insert(prompt[j], prompt[j + 1:j + N], prompt[j - 1] if j else -1)
+    prev = int(prompt[-2]) if len(prompt) >= 2 else -1       # token before cur
     win = np.asarray(init_window, dtype=np.int64).reshape(N - 1, W).copy()
     M = n_rows(N, W, G)
     bmask = block_mask(N, W, G)
@@ -419,7 +444,7 @@ def lookahead(model: OracleModel, prompt, N: int, W: int, G: int, max_new: int,
     res = DecodeResult([], 0, [], [], [], [], pool)
     while len(out) < max_new:
         # (3) selection: n-grams whose first token is the last output token
-        cands = pool.select(cur, G)
+        cands = pool.select(cur, G, prev if pool_context else None)
         # block rows (R1), unused candidate slots hold token 0 (R8)
         toks = np.zeros(M, dtype=np.int64)
         toks[0] = cur
@@ -455,8 +480,8 @@ def lookahead(model: OracleModel, prompt, N: int, W: int, G: int, max_new: int,
 
         # lookahead branch: new tokens = outputs of the newest level
         new = np.array([a[1 + (N - 2) * W + k] for k in range(W)], dtype=np.int64)
-        for gram in harvest(win, new):
-            pool.insert(gram[0], gram[1:])
+        for k, gram in enumerate(harvest(win, new)):
+            pool.insert(gram[0], gram[1:], win[0, k - 1] if k else cur)   # R22 context
         win = slide(win, new)
 
         # emit, truncated to the budget / at EOS (R10)
@@ -468,6 +493,7 @@ def lookahead(model: OracleModel, prompt, N: int, W: int, G: int, max_new: int,
         res.steps += 1
         res.accepted.append(acc)
         res.emitted.append(len(step_emit))
+        prev = int(emit[-2]) if len(emit) >= 2 else int(cur)
         cur = bonus
         if eos_id >= 0 and out and out[-1] == eos_id:
             break

@@ -284,6 +284,75 @@ def test_pool_lru_is_recency_order():
         assert p.evictions == 0
 
 
+def test_pool_context_selection_by_hand():
+    """R22 worked by hand: bucket a(7) b(3) c(7) d(1), oldest first, G = 2."""
+    p = la.NGramPool(8)
+    for sfx, ctx in [((1,), 7), ((2,), 3), ((3,), 7), ((4,), 1)]:
+        p.insert(9, sfx, ctx)
+    assert p.select(9, 2) == [(3,), (4,)]                 # R6: the newest two
+    assert p.select(9, 2, prev=7) == [(1,), (3,)]         # both context-7 entries
+    assert p.select(9, 2, prev=3) == [(2,), (4,)]         # b, then the newest other (d)
+    assert p.select(9, 3, prev=5) == [(2,), (3,), (4,)]   # no match: the newest three
+    p.insert(9, (1,), 5)                                  # a repeat takes the new context
+    assert p.context[(9, (1,))] == 5 and p.select(9, 1, prev=5) == [(1,)]
+    p2 = la.NGramPool(2)
+    for sfx in [(1,), (2,), (3,)]:
+        p2.insert(0, sfx, 4)
+    assert set(p2.context) == {(0, (2,)), (0, (3,))}      # an evicted entry's context goes too
+
+
+def test_pool_context_selection_properties():
+    """Without a matching context, or when the bucket fits in G, selection by
+    context takes the same set as R6."""
+    rng = np.random.default_rng(6)
+    for _ in range(200):
+        cap, G = int(rng.integers(1, 8)), int(rng.integers(1, 8))
+        p = la.NGramPool(cap)
+        for _ in range(int(rng.integers(1, 20))):
+            p.insert(0, (int(rng.integers(6)),), int(rng.integers(3)))
+        b = p.buckets[0]
+        assert p.select(0, G, prev=99) == p.select(0, G)
+        if len(b) <= G:
+            assert p.select(0, G, prev=int(rng.integers(3))) == b
+
+
+def test_prompt_ngram_contexts():
+    """Prompt n-grams (R11) carry the prompt token before them (none for the
+    first); a repeated n-gram keeps its last occurrence's context."""
+    s = synth.SHAPES["micro"]
+    om = OracleModel(s, synth.gen_weights(s, 0))
+    prompt = np.array([1, 2, 3, 4, 1, 2, 3, 5, 1, 2, 3, 4, 6], dtype=np.int64)
+    N = 3
+    r = la.lookahead(om, prompt, N, 0, 4, 1, np.zeros((N - 1, 0), dtype=np.int64),
+                     prompt_ref=True, pool_cap=16, pool_context=True)
+    want = {}
+    for j in range(len(prompt) - N + 1):
+        want[(int(prompt[j]), tuple(int(t) for t in prompt[j + 1:j + N]))] = \
+            int(prompt[j - 1]) if j else -1
+    got = {k: v for k, v in r.pool.context.items() if k in want}
+    assert got == want
+
+
+@pytest.mark.parametrize("N,W,G,cap,lru", [(4, 5, 5, 20, False), (4, 5, 5, 10, True),
+                                           (3, 4, 2, 8, False), (5, 3, 3, 3, False)])
+def test_lookahead_context_selection_is_exact(N, W, G, cap, lru):
+    """Selection by context only changes which guesses are verified: the
+    output equals greedy AR; with cap <= G it changes nothing at all."""
+    s = synth.SHAPES["micro"]
+    om = OracleModel(s, synth.gen_weights(s, 0))
+    for seed in range(3):
+        prompt = synth.prompt_motif(s.vocab, seed=seed)
+        win = synth.gen_window(N, W, s.vocab, seed=2)
+        ref = la.greedy_ar(om, prompt, 64).tokens
+        r = la.lookahead(om, prompt, N, W, G, 64, win, prompt_ref=True, pool_cap=cap,
+                         pool_lru=lru, pool_context=True)
+        assert r.tokens == ref
+        if cap <= G:
+            f = la.lookahead(om, prompt, N, W, G, 64, win, prompt_ref=True, pool_cap=cap,
+                             pool_lru=lru)
+            assert f.accepted == r.accepted
+
+
 @pytest.mark.parametrize("N,W,G,cap", [(3, 4, 4, None), (4, 5, 3, 2), (5, 3, 3, 1)])
 def test_lookahead_lru_pool_is_exact(N, W, G, cap):
     """The pool's policy only changes which guesses are verified, never the
