@@ -60,8 +60,9 @@ def parse():
     ap.add_argument("--pool-cap", type=int, default=0,
                     help="suffixes kept per first token (0 = G)")
     ap.add_argument("--pool-study", action="store_true",
-                    help="instead: step compression S against the pool cap and eviction policy "
-                         "(FIFO, recency) on the small random-init models whose greedy output "
+                    help="instead: step compression S against the pool cap, eviction policy "
+                         "(FIFO, recency) and selection rule (newest, by context) on the small "
+                         "random-init models whose greedy output "
                          "repeats n-grams (micro, tiny), eight motif prompts each")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the benchmark line: step time against the row count "
@@ -339,8 +340,9 @@ def gemm_bench(shape, rows, read_gbps, reps=10):
 
 
 def pool_study(N=4, W=5, G=5, n_new=128, seeds=8):
-    """S = tokens / steps of whole generations against the pool cap and its
-    eviction policy, on the random-init micro (vocab 8) and tiny (vocab 256)
+    """S = tokens / steps of whole generations against the pool cap, its
+    eviction policy and the candidate selection rule (the newest G, or by
+    context first), on the random-init micro (vocab 8) and tiny (vocab 256)
     models, whose greedy continuations of a repeated-motif prompt repeat
     n-grams (the 7B-shape random model repeats none, so its S is 1 under any
     pool).  Also checks that every generation equals the same engine's AR
@@ -357,24 +359,26 @@ def pool_study(N=4, W=5, G=5, n_new=128, seeds=8):
             ses = model.session(pr, N, W, G, n_new, ar=True)
             ar.append(ses.decode())
             ses.close()
-        for cap in (1, 2, G, 2 * G, 4 * G):
-            for lru in (False, True):
-                S, ev, exact = [], 0, True
-                for pr, ref in zip(prompts, ar):
-                    ses = model.session(pr, N, W, G, n_new, window=win, prompt_ref=True,
-                                        pool_cap=cap, pool_lru=lru)
-                    toks = ses.decode()
-                    st = ses.stats()
-                    ses.close()
-                    exact = exact and toks == ref
-                    S.append(st["tokens"] / st["steps"])
-                    ev += st["evictions"]
-                print(json.dumps({"study": "pool cap and eviction policy", "shape": name,
-                                  "N": N, "W": W, "G": G, "new_tokens": n_new, "pool_cap": cap,
-                                  "policy": "lru" if lru else "fifo", "S_mean": sum(S) / len(S),
-                                  "S_per_prompt": [round(v, 4) for v in S],
-                                  "evictions_total": ev, "lookahead_equals_ar": exact}),
-                      flush=True)
+        for cap, lru, ctx in [(c, l, x) for c in (1, 2, G, 2 * G, 4 * G) for l in (False, True)
+                              for x in (False, True)]:
+            S, ev, exact = [], 0, True
+            for pr, ref in zip(prompts, ar):
+                ses = model.session(pr, N, W, G, n_new, window=win, prompt_ref=True,
+                                    pool_cap=cap, pool_lru=lru, pool_context=ctx)
+                toks = ses.decode()
+                st = ses.stats()
+                ses.close()
+                exact = exact and toks == ref
+                S.append(st["tokens"] / st["steps"])
+                ev += st["evictions"]
+            print(json.dumps({"study": "pool cap and eviction policy", "shape": name,
+                              "N": N, "W": W, "G": G, "new_tokens": n_new, "pool_cap": cap,
+                              "policy": "lru" if lru else "fifo",
+                              "selection": "context" if ctx else "newest",
+                              "S_mean": sum(S) / len(S),
+                              "S_per_prompt": [round(v, 4) for v in S],
+                              "evictions_total": ev, "lookahead_equals_ar": exact}),
+                  flush=True)
         model.close()
 
 

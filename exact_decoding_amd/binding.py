@@ -19,7 +19,7 @@ LA_EINVAL, LA_ENOMEM, LA_ECTX, LA_EHIP, LA_ESTATE = -1, -2, -3, -4, -5
 LA_F32, LA_BF16 = 0, 1
 LA_MAX_N = 16
 LA_PROBE_BLOCKS = 2048
-LA_PROMPT_REF, LA_AR, LA_NO_GRAPH, LA_POOL_LRU = 1, 2, 8, 16
+LA_PROMPT_REF, LA_AR, LA_NO_GRAPH, LA_POOL_LRU, LA_POOL_CONTEXT = 1, 2, 8, 16, 32
 
 EXPORTS = [
     "la_model_load", "la_model_free", "la_session_bytes", "la_prefill", "la_step",

@@ -36,18 +36,24 @@ namespace {
 __device__ __forceinline__ int32_t* bucket(const PoolDesc& p, int key, int e) {
   return p.tok + ((size_t)key * p.cap + e) * p.n1;
 }
+__device__ __forceinline__ int32_t& ctx_of(const PoolDesc& p, int key, int e) {
+  return p.ctx[(size_t)key * p.cap + e];
+}
 
 struct InsertCounts {
   int ins, dup, ev, ngr, keys;
 };
 
-// Insert (key, sfx[0..n1)) into the pool; one thread.  A bucket is a ring
-// of cap entries, oldest at head.  A suffix already present is counted as a
-// repeat and, with lru, moved to the newest end (the entries after it move
-// one place towards the head), so that eviction drops the suffix generated
-// least recently ([LD] "Memory-efficient n-gram pool management" names LRU
-// and FIFO as the policies to compare; FIFO leaves it in place).
-__device__ void pool_insert(const PoolDesc& p, int key, const int32_t* sfx, InsertCounts& c) {
+// Insert (key, sfx[0..n1)) with context token ctx (the token before the
+// n-gram, -1 for none) into the pool; one thread.  A bucket is a ring of cap
+// entries, oldest at head.  A suffix already present is counted as a repeat
+// and takes the new context; with lru it also moves to the newest end (the
+// entries after it move one place towards the head), so that eviction drops
+// the suffix generated least recently ([LD] "Memory-efficient n-gram pool
+// management" names LRU and FIFO as the policies to compare; FIFO leaves it
+// in place).
+__device__ void pool_insert(const PoolDesc& p, int key, const int32_t* sfx, int ctx,
+                            InsertCounts& c) {
   const int cnt = p.cnt[key];
   const int head = p.head[key];
   for (int e = 0; e < cnt; ++e) {
@@ -67,12 +73,15 @@ __device__ void pool_insert(const PoolDesc& p, int key, const int32_t* sfx, Inse
           int32_t* dst = bucket(p, key, to);
           const int32_t* src = bucket(p, key, from);
           for (int i = 0; i < p.n1; ++i) dst[i] = src[i];
+          ctx_of(p, key, to) = ctx_of(p, key, from);
         }
         int last = head + cnt - 1;
         if (last >= p.cap) last -= p.cap;
         int32_t* dst = bucket(p, key, last);
         for (int i = 0; i < p.n1; ++i) dst[i] = sfx[i];
+        idx = last;
       }
+      ctx_of(p, key, idx) = ctx;
       return;
     }
   }
@@ -91,34 +100,61 @@ __device__ void pool_insert(const PoolDesc& p, int key, const int32_t* sfx, Inse
   }
   int32_t* b = bucket(p, key, idx);
   for (int i = 0; i < p.n1; ++i) b[i] = sfx[i];
+  ctx_of(p, key, idx) = ctx;
 }
 
+// Candidate g of the step is bucket entry s_sel[g] (ring index): the newest
+// G entries in bucket order, or, selecting by context, the newest entries
+// whose context is the token before cur and then the newest of the rest,
+// still in bucket order (one thread marks them walking from the newest end).
+constexpr int GATHER_MAX_G = 1024;
 __global__ __launch_bounds__(256) void k_gather(PoolDesc pool, StepIO io, RowLayout L) {
-  __shared__ int s_take, s_first;
+  __shared__ int s_take;
+  __shared__ int s_sel[GATHER_MAX_G];
   DevState* st = io.st;
   const int cur = st->cur, P = st->P;
   const int n1 = L.N - 1;
   if (threadIdx.x == 0) {
     const int cnt = L.G > 0 ? pool.cnt[cur] : 0;
     const int take = cnt < L.G ? cnt : L.G;
+    const int head = pool.head[cur];
     s_take = take;
-    int first = pool.head[cur] + (cnt - take);
-    if (first >= pool.cap) first -= pool.cap;
-    s_first = first;
+    if (!pool.by_ctx || take == cnt) {
+      for (int g = 0; g < take; ++g) {
+        int e = head + (cnt - take) + g;
+        if (e >= pool.cap) e -= pool.cap;
+        s_sel[g] = e;
+      }
+    } else {
+      // the bucket position (0 = oldest) of the entries taken, in bucket
+      // order: first count the matches among the newest, then merge
+      const int prev = st->prev;
+      int nm = 0;
+      for (int j = cnt - 1; j >= 0 && nm < take; --j) {
+        int e = head + j;
+        if (e >= pool.cap) e -= pool.cap;
+        nm += ctx_of(pool, cur, e) == prev;
+      }
+      // take the nm newest matches and the take - nm newest others
+      int need_m = nm, need_o = take - nm, g = take;
+      for (int j = cnt - 1; j >= 0 && g > 0; --j) {
+        int e = head + j;
+        if (e >= pool.cap) e -= pool.cap;
+        const bool m = ctx_of(pool, cur, e) == prev;
+        if (m && need_m > 0) { s_sel[--g] = e; --need_m; }
+        else if (!m && need_o > 0) { s_sel[--g] = e; --need_o; }
+      }
+    }
     st->ncand = take;
     st->stats[ST_GATHER_NE] += take > 0;
     st->stats[ST_CAND_TOTAL] += take;
   }
   __syncthreads();
-  const int take = s_take, first = s_first;
+  const int take = s_take;
   for (int u = threadIdx.x; u < L.G * n1; u += blockDim.x) {
     const int g = u / n1, i = u - g * n1;
     int v = 0;  // unused candidate slots hold token 0
-    if (g < take) {
-      int e = first + g;
-      if (e >= pool.cap) e -= pool.cap;
-      v = bucket(pool, cur, e)[i];
-    }
+    if (g < take) v = bucket(pool, cur, s_sel[g])[i];
     io.cand[u] = v;
     io.ids[1 + L.W * n1 + u] = v;
     io.pos[1 + L.W * n1 + u] = P + i + 1;
@@ -144,6 +180,7 @@ __global__ __launch_bounds__(64) void k_verify(PoolDesc pool, StepIO io, RowLayo
   DevState* st = io.st;
   const int lane = threadIdx.x;
   const int n1 = L.N - 1, W = L.W, G = L.G, M = L.M;
+  const int cur_old = io.ids[0];  // the step's current token (row 0)
   for (int i = lane; i < M; i += 64) a[i] = io.amax[i];
   for (int i = lane; i < G * n1; i += 64) cand[i] = io.cand[i];
   for (int i = lane; i < W * n1; i += 64) win[i] = io.win[i];
@@ -186,6 +223,13 @@ __global__ __launch_bounds__(64) void k_verify(PoolDesc pool, StepIO io, RowLayo
     st->stats[ST_STEPS] += 1;
     st->stats[ST_TOKENS] += n;
   }
+  if (lane == 0) {
+    // the token before the new cur: the second to last emitted, or the old
+    // cur when one token was emitted (greedy above, or sampling verification
+    // before this kernel); a truncated step ends the session
+    const int n = st->n_out;
+    st->prev = n >= 2 ? st->out[n - 2] : cur_old;
+  }
 
   // lookahead branch: harvest one n-gram per column (oldest level .. newest,
   // then the column's new token) and insert in column order.  Columns sharing
@@ -202,7 +246,8 @@ __global__ __launch_bounds__(64) void k_verify(PoolDesc pool, StepIO io, RowLayo
         if (win[k2] != key) continue;
         for (int l = 1; l < n1; ++l) sfx[l - 1] = win[l * W + k2];
         sfx[n1 - 1] = a[1 + (n1 - 1) * W + k2];
-        pool_insert(pool, key, sfx, c);
+        // context: the level-0 token to the column's left, or the step's cur
+        pool_insert(pool, key, sfx, k2 > 0 ? win[k2 - 1] : cur_old, c);
       }
     }
   }
@@ -623,7 +668,8 @@ __global__ __launch_bounds__(256) void k_kv_commit(KvCommit c) {
 __global__ void k_pool_seed(PoolDesc pool, DevState* st, const int32_t* prompt, int n) {
   if (threadIdx.x != 0 || blockIdx.x != 0) return;
   InsertCounts c = {0, 0, 0, 0, 0};
-  for (int j = 0; j + pool.n1 < n; ++j) pool_insert(pool, prompt[j], prompt + j + 1, c);
+  for (int j = 0; j + pool.n1 < n; ++j)
+    pool_insert(pool, prompt[j], prompt + j + 1, j > 0 ? prompt[j - 1] : -1, c);
   st->stats[ST_INSERTS] += c.ins;
   st->stats[ST_DUPS] += c.dup;
   st->stats[ST_EVICT] += c.ev;
@@ -669,6 +715,7 @@ hipError_t launch_probe_read(const void* buf, size_t bytes, uint32_t* out, hipSt
 
 hipError_t launch_gather(const PoolDesc& pool, const StepIO& io, const RowLayout& lay,
                          hipStream_t st) {
+  if (lay.G > GATHER_MAX_G) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_gather, dim3(1), dim3(256), 0, st, pool, io, lay);
   return hipGetLastError();
 }

@@ -75,13 +75,13 @@ struct WsPlan {
 
 struct Views {
   size_t x, h, q, att, att_part, act, part, logits, amax, kc, vc, kb, vb, rope, pool_tok, pool_cnt,
-      pool_head, win, cand, ids, pos, prompt, st, total;
+      pool_head, pool_ctx, win, cand, ids, pos, prompt, st, total;
 };
 
 struct Shape {
   int L, d, H, Hkv, hd, F, V, dt;
   int M, rows_cap, ld_ctx;
-  int N, W, G, cap, lru;
+  int N, W, G, cap, lru, by_ctx;
   SplitPlan sp_qkv, sp_o, sp_gu, sp_d, sp_lm;
   double pc_qkv, pc_o, pc_gu, pc_d;  // mean pieces per column block (profile bytes)
   int att_mfma, att_nsplit;  // MFMA-attention prefix chunks (0 = per-row kernel only)
@@ -98,6 +98,7 @@ Shape make_shape(const la_model* m, const la_decode_params* p) {
   s.G = ar ? 0 : p->G;
   s.cap = p->pool_cap > 0 ? p->pool_cap : (s.G > 0 ? s.G : 1);
   s.lru = (p->flags & LA_POOL_LRU) != 0;
+  s.by_ctx = (p->flags & LA_POOL_CONTEXT) != 0;
   s.M = 1 + (s.W + s.G) * (s.N - 1);
   s.ld_ctx = p->max_ctx;
   s.rows_cap = s.M > p->max_ctx ? s.M : p->max_ctx;
@@ -157,6 +158,7 @@ Views plan_views(const Shape& s) {
   v.pool_tok = w.take((size_t)s.V * s.cap * n1 * 4);
   v.pool_cnt = w.take((size_t)s.V * 4);
   v.pool_head = w.take((size_t)s.V * 4);
+  v.pool_ctx = w.take((size_t)s.V * s.cap * 4);
   v.win = w.take((size_t)(s.W * n1 > 0 ? s.W * n1 : 1) * 4);
   v.cand = w.take((size_t)(s.G * n1 > 0 ? s.G * n1 : 1) * 4);
   v.ids = w.take(R * 4);
@@ -173,10 +175,11 @@ int check_params(const la_model* m, const la_decode_params* p) {
   if (p->N < 2 || p->N > LA_MAX_N) return fail(LA_EINVAL, "N must be in [2, 16]");
   if (!ar && (p->W < 0 || p->G < 0)) return fail(LA_EINVAL, "W and G must be >= 0");
   if (p->pool_cap < 0 || p->pool_cap > 4096) return fail(LA_EINVAL, "pool_cap out of range");
+  if (!ar && p->G > 1024) return fail(LA_EINVAL, "G must be <= 1024");
   if (p->max_ctx < 2) return fail(LA_EINVAL, "max_ctx must be >= 2");
   if (p->max_new < 1) return fail(LA_EINVAL, "max_new must be >= 1");
   if (p->eos_id >= m->d.vocab) return fail(LA_EINVAL, "eos_id out of range");
-  if (p->flags & ~(LA_PROMPT_REF | LA_AR | LA_NO_GRAPH | LA_POOL_LRU)) return fail(LA_EINVAL, "unknown flags");
+  if (p->flags & ~(LA_PROMPT_REF | LA_AR | LA_NO_GRAPH | LA_POOL_LRU | LA_POOL_CONTEXT)) return fail(LA_EINVAL, "unknown flags");
   const long long W = ar ? 0 : p->W, G = ar ? 0 : p->G;
   const long long M = 1 + (W + G) * (p->N - 1);
   if (M > 2048) return fail(LA_EINVAL, "1 + (W+G)(N-1) must be <= 2048");
@@ -406,7 +409,8 @@ int enqueue_step(la_session* ss) {
   hipStream_t st = ss->stream;
   const int dt = s.dt;
   PoolDesc pool{ss->at<int32_t>(ss->v.pool_tok), ss->at<int32_t>(ss->v.pool_cnt),
-                ss->at<int32_t>(ss->v.pool_head), s.V, s.cap, s.N - 1, s.lru};
+                ss->at<int32_t>(ss->v.pool_head), s.V, s.cap, s.N - 1, s.lru,
+                ss->at<int32_t>(ss->v.pool_ctx), s.by_ctx};
   StepIO io{};
   io.st = ss->at<DevState>(ss->v.st);
   io.win = ss->at<int32_t>(ss->v.win);
@@ -613,6 +617,7 @@ int la_prefill(la_model* m, const la_decode_params* p, const int32_t* prompt, in
   memset(&h0, 0, sizeof(h0));
   h0.P = n_prompt - 1;
   h0.cur = prompt[n_prompt - 1];
+  h0.prev = n_prompt >= 2 ? prompt[n_prompt - 2] : -1;
 
   LA_PF(hipMemcpyAsync(ss->at(v.rope), rope.data(), rope.size() * sizeof(float2), hipMemcpyHostToDevice, st));
   LA_PF(hipMemcpyAsync(ss->at(v.prompt), prompt, (size_t)n_prompt * 4, hipMemcpyHostToDevice, st));
@@ -631,7 +636,8 @@ int la_prefill(la_model* m, const la_decode_params* p, const int32_t* prompt, in
   }
   if ((p->flags & LA_PROMPT_REF) && s.G > 0 && n_prompt >= s.N) {
     PoolDesc pool{ss->at<int32_t>(v.pool_tok), ss->at<int32_t>(v.pool_cnt),
-                  ss->at<int32_t>(v.pool_head), s.V, s.cap, n1, s.lru};
+                  ss->at<int32_t>(v.pool_head), s.V, s.cap, n1, s.lru,
+                  ss->at<int32_t>(v.pool_ctx), s.by_ctx};
     LA_PF(launch_pool_seed(pool, ss->at<DevState>(v.st), ss->at<int32_t>(v.prompt), n_prompt, st));
   }
   LA_PF(hipStreamSynchronize(st));

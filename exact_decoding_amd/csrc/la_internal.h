@@ -47,7 +47,8 @@ struct DevState {
   int32_t commit_p;    // P before the last step's commit
   int32_t commit_n;    // rows committed by the last step
   int32_t commit_rows[LA_MAX_N];
-  int32_t pad_[3];
+  int32_t prev;        // the token before cur (-1: none)
+  int32_t pad_[2];
   long long stats[ST_COUNT];
 };
 
@@ -191,6 +192,8 @@ struct PoolDesc {
   int32_t* head;  // [V]
   int V, cap, n1; // n1 = N - 1
   int lru;        // 1: a repeated suffix becomes the bucket's newest entry
+  int32_t* ctx;   // [V][cap] the token before each entry's n-gram (-1: none)
+  int by_ctx;     // 1: select entries whose context is the token before cur first
 };
 struct StepIO {
   DevState* st;

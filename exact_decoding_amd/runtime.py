@@ -67,14 +67,17 @@ class Model:
                 prompt_ref: bool = False, ar: bool = False, graph: bool = True,
                 max_ctx: int | None = None, pool_cap: int = 0, eos_id: int = -1,
                 temperature: float = 0.0, seed: int = 0, top_k: int = 0,
-                top_p: float = 0.0, pool_lru: bool = False) -> "Session":
+                top_p: float = 0.0, pool_lru: bool = False,
+                pool_context: bool = False) -> "Session":
         """temperature 0: greedy; > 0: sampling verification with draws keyed
         by `seed`, optionally cut to the top_k tokens and then to a top_p share
         (0 = no cut; see la.h).  pool_lru: evict pool entries by recency
-        instead of FIFO (LA_POOL_LRU)."""
+        instead of FIFO (LA_POOL_LRU); pool_context: select candidates by
+        their context token first (LA_POOL_CONTEXT)."""
         flags = (B.LA_PROMPT_REF if prompt_ref else 0) | (B.LA_AR if ar else 0)
         flags |= 0 if graph else B.LA_NO_GRAPH
         flags |= B.LA_POOL_LRU if pool_lru else 0
+        flags |= B.LA_POOL_CONTEXT if pool_context else 0
         if max_ctx is None:
             max_ctx = len(prompt) + max_new + N + W + 2
         p = B.DecodeParams(N, W, G, pool_cap, max_ctx, max_new, eos_id, flags,

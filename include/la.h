@@ -59,7 +59,7 @@ typedef struct {
  * N  n-gram length (2..LA_MAX_N); the window has N-1 levels ([LD] §3.4
  *    "The Lookahead Branch").
  * W  window width (columns), >= 0.
- * G  max verification candidates per step, >= 0 ([LD] §3.4 "N-gram
+ * G  max verification candidates per step, 0..1024 ([LD] §3.4 "N-gram
  *    selection from the pool").
  * pool_cap   suffixes kept per first token; 0 means G (min 1).
  * max_ctx    KV-cache capacity in positions.
@@ -80,6 +80,16 @@ typedef struct {
  *              "Memory-efficient n-gram pool management").  Selection (the
  *              newest G of the bucket) and the output tokens are unchanged;
  *              repeats are still counted in dup_skips.
+ *            LA_POOL_CONTEXT: select by a longer match.  Every entry keeps
+ *              the token just before its n-gram where it was generated (for
+ *              a window column the level-0 token of the column to its left,
+ *              or the step's current token; for a prompt n-gram the prompt
+ *              token before it).  The G candidates are then the newest
+ *              entries whose context equals the token before the current
+ *              one, then the newest of the rest, in the bucket's order.  The
+ *              pages contrast first-token matching with longer prefixes
+ *              ([LD] Table 3, "What is not ablated").  Output tokens are
+ *              unchanged; it matters only when pool_cap > G.
  * temperature  0: greedy verification ([LD] §3.4 "Greedy verification
  *              algorithm (Algorithm 3)").  > 0: sampling verification
  *              ([LD] §3.4 "Sampling verification (Algorithm 4)") against
@@ -112,6 +122,7 @@ typedef struct {
 #define LA_AR 2u
 #define LA_NO_GRAPH 8u
 #define LA_POOL_LRU 16u
+#define LA_POOL_CONTEXT 32u
 
 /* Statistics since prefill ([LD] §3.4 "Scaling Law": S = tokens / steps). */
 typedef struct {

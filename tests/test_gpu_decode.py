@@ -277,3 +277,41 @@ def test_micro_lru_pool_matches_oracle(micro, N, W, G, cap, graph):
         stats[lru] = got
     if (N, W, G) == (3, 4, 4):
         assert stats[True] != stats[False]
+
+
+@pytest.mark.parametrize("N,W,G,cap,lru", [(4, 5, 5, 20, False), (4, 5, 5, 10, True),
+                                           (3, 4, 2, 8, False)])
+def test_micro_context_selection_matches_oracle(micro, N, W, G, cap, lru):
+    """Selection by context (LA_POOL_CONTEXT) with a pool cap above G, where
+    it changes which candidates are verified: for two motif prompts the GPU
+    emits the greedy AR tokens in the oracle's steps, with its accepted-length
+    histogram and pool counters.  The oracle's block rows of these runs have
+    top-2 margins above 1e-3 (checked here), far above the fp32 error.  At
+    (4, 5, 5, cap 20) selection by context takes fewer steps than the newest-G
+    rule for prompt 0, so the selection path is exercised."""
+    s, w, gm, om = micro
+    n_new = 64
+    win = synth.gen_window(N, W, s.vocab, seed=2)
+    for seed in (0, 2):
+        prompt = synth.prompt_motif(s.vocab, seed=seed)
+        print(f"micro context N={N} W={W} G={G} cap={cap} lru={lru} prompt={seed}", flush=True)
+        ar = la.greedy_ar(om, prompt, n_new)
+        ref = la.lookahead(om, prompt, N, W, G, n_new, win, prompt_ref=True, pool_cap=cap,
+                           pool_lru=lru, pool_context=True, keep_logits=True)
+        margin = min(float((np.sort(l, axis=1)[:, -1] - np.sort(l, axis=1)[:, -2]).min())
+                     for l in ref.step_logits)
+        assert margin > 1e-3
+        assert ref.tokens == ar.tokens
+        ses = gm.session(prompt, N, W, G, n_new, window=win, prompt_ref=True, pool_cap=cap,
+                         pool_lru=lru, pool_context=True)
+        toks = ses.decode()
+        st = ses.stats()
+        ses.close()
+        assert toks == ar.tokens
+        assert st["steps"] == ref.steps
+        assert [st["accept_hist"][j] for j in range(N)] == [ref.accepted.count(j) for j in range(N)]
+        assert (st["inserts"], st["dup_skips"], st["evictions"], st["pool_ngrams"]) == \
+            (ref.pool.inserts, ref.pool.dup_skips, ref.pool.evictions, ref.pool.n_ngrams())
+        if (N, W, G, cap, lru, seed) == (4, 5, 5, 20, False, 0):
+            plain = la.lookahead(om, prompt, N, W, G, n_new, win, prompt_ref=True, pool_cap=cap)
+            assert plain.steps != ref.steps

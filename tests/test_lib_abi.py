@@ -31,7 +31,8 @@ def test_flag_values_match_header():
     src = open(os.path.join(ROOT, "include", "la.h")).read()
     defs = dict(re.findall(r"#define (LA_[A-Z_]+) (\d+)u", src))
     assert defs == {"LA_PROMPT_REF": str(B.LA_PROMPT_REF), "LA_AR": str(B.LA_AR),
-                    "LA_NO_GRAPH": str(B.LA_NO_GRAPH), "LA_POOL_LRU": str(B.LA_POOL_LRU)}
+                    "LA_NO_GRAPH": str(B.LA_NO_GRAPH), "LA_POOL_LRU": str(B.LA_POOL_LRU),
+                    "LA_POOL_CONTEXT": str(B.LA_POOL_CONTEXT)}
 
 
 def _model(dtype=B.LA_BF16, L=2, d=512, H=4, Hkv=4, hd=128, F=1408, V=4000):
@@ -71,7 +72,8 @@ def test_session_bytes_and_param_validation():
     p_s = B.DecodeParams(5, 15, 15, 0, 400, 256, -1, B.LA_PROMPT_REF, 0.8, 0, 12345)
     assert B.la_session_bytes(m, p_s) == n
     # nor does the pool's eviction policy
-    p_l = B.DecodeParams(5, 15, 15, 0, 400, 256, -1, B.LA_PROMPT_REF | B.LA_POOL_LRU)
+    p_l = B.DecodeParams(5, 15, 15, 0, 400, 256, -1,
+                         B.LA_PROMPT_REF | B.LA_POOL_LRU | B.LA_POOL_CONTEXT)
     assert B.la_session_bytes(m, p_l) == n
     # nor do top-K / top-P (K past the vocabulary and p = 1 are no cut)
     for k, pp in [(40, 0.9), (1, 0.0), (10 ** 6, 1.0)]:
@@ -80,7 +82,8 @@ def test_session_bytes_and_param_validation():
     for bad in [B.DecodeParams(1, 4, 4, 0, 100, 10, -1, 0), B.DecodeParams(17, 4, 4, 0, 100, 10, -1, 0),
                 B.DecodeParams(3, -1, 4, 0, 100, 10, -1, 0), B.DecodeParams(3, 4, 4, 0, 100, 0, -1, 0),
                 B.DecodeParams(3, 4, 4, 0, 100, 10, 4000, 0), B.DecodeParams(3, 4, 4, 0, 100, 10, -1, 64),
-                B.DecodeParams(3, 4, 4, 0, 100, 10, -1, 32),
+                B.DecodeParams(3, 4, 4, 0, 100, 10, -1, 64 * 2),
+                B.DecodeParams(2, 0, 1025, 0, 4000, 10, -1, 0),
                 B.DecodeParams(16, 100, 100, 0, 100, 10, -1, 0),
                 # sampling: negative or non-finite temperature, reserved field set
                 B.DecodeParams(3, 4, 4, 0, 100, 10, -1, 0, -0.5, 0, 1),
