@@ -379,6 +379,31 @@ def pool_study(N=4, W=5, G=5, n_new=128, seeds=8):
                               "S_per_prompt": [round(v, 4) for v in S],
                               "evictions_total": ev, "lookahead_equals_ar": exact}),
                   flush=True)
+        # wall clock of whole generations (graph replay, default pool): does
+        # the compression turn into tokens/s over the same engine's AR decode?
+        import torch
+
+        def timed(make):
+            sessions = [make(pr) for pr in prompts]  # prefilled before the clock
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            n = sum(len(ses.decode()) for ses in sessions)
+            torch.cuda.synchronize()
+            dt = time.perf_counter() - t0
+            steps = sum(ses.stats()["steps"] for ses in sessions)
+            for ses in sessions:
+                ses.close()
+            return n / dt, dt * 1e3 / steps, n / steps
+
+        for _ in range(2):  # the first round warms the graphs and caches
+            la_tps, la_ms, la_S = timed(lambda pr: model.session(pr, N, W, G, n_new, window=win,
+                                                                 prompt_ref=True))
+            ar_tps, ar_ms, _ = timed(lambda pr: model.session(pr, N, W, G, n_new, ar=True))
+        print(json.dumps({"study": "lookahead vs AR wall clock", "shape": name, "N": N, "W": W,
+                          "G": G, "new_tokens": n_new, "prompts": seeds, "S": la_S,
+                          "lookahead_tokens_per_s": la_tps, "ar_tokens_per_s": ar_tps,
+                          "speedup": la_tps / ar_tps, "lookahead_ms_per_step": la_ms,
+                          "ar_ms_per_step": ar_ms}), flush=True)
         model.close()
 
 
