@@ -54,7 +54,7 @@ R21 Pool eviction by recency (the pages leave the pool's size cap and its
     takes the newest G in the bucket's order under either policy.
 R22 Selection by a longer match (the pages contrast matching only the first
     token with matching longer prefixes, and note that the prompt-lookup
-    baseline checks several starting tokens, [LD] Table 3 and "What is not
+    baseline tries more than one starting token, [LD] Table 3 and "What is not
     ablated"): every entry also keeps its context, the token just before the
     n-gram's first token where it was generated (a window column's context
     is the level-0 token of the column to its left, or the step's current
