@@ -315,3 +315,25 @@ def test_micro_context_selection_matches_oracle(micro, N, W, G, cap, lru):
         if (N, W, G, cap, lru, seed) == (4, 5, 5, 20, False, 0):
             plain = la.lookahead(om, prompt, N, W, G, n_new, win, prompt_ref=True, pool_cap=cap)
             assert plain.steps != ref.steps
+
+
+@pytest.mark.parametrize("graph", [True, False])
+def test_bf16_pool_variants_bit_exact(graph):
+    """The pool variants change only which guesses are verified: with a cap
+    above G, recency eviction and selection by context, the bf16 model's
+    lookahead stream still equals the same engine's AR stream bit for bit."""
+    s = synth.SHAPES["small_bf16"]
+    gm = Model(s, synth.gen_weights(s, 0))
+    prompt = synth.prompt_zipf_spans(s.vocab, length=64, seed=1)
+    N, W, G, n_new = 5, 7, 7, 48
+    win = synth.gen_window(N, W, s.vocab, seed=2)
+    ar = gm.session(prompt, N, W, G, n_new, ar=True, graph=graph)
+    ar_toks = ar.decode()
+    ar.close()
+    for lru, ctx in ((True, False), (False, True), (True, True)):
+        print(f"bf16 pool variant lru={lru} context={ctx} graph={graph}", flush=True)
+        ses = gm.session(prompt, N, W, G, n_new, window=win, prompt_ref=True, graph=graph,
+                         pool_cap=3 * G, pool_lru=lru, pool_context=ctx)
+        assert ses.decode() == ar_toks
+        ses.close()
+    gm.close()

@@ -285,3 +285,33 @@ def test_bf16_top1_and_vanishing_top_p_are_greedy():
         assert ar.decode() == greedy
         ar.close()
     gm.close()
+
+
+@pytest.mark.parametrize("lru,ctx", [(True, False), (False, True), (True, True)])
+def test_micro_sampling_pool_variants_match_oracle(micro, lru, ctx):
+    """Sampling verification with the pool variants and a cap above G: the
+    candidates the sampling kernel accepts set the token before cur for the
+    next selection by context; while decided, the GPU matches the oracle's
+    tokens and, for a fully decided run, its pool counters."""
+    s, w, gm, om = micro
+    N, W, G, n_new, T = 3, 3, 3, 24, 0.7
+    compared = 0
+    for seed in range(4):
+        print(f"micro sampling pool lru={lru} context={ctx} seed={seed}", flush=True)
+        win = synth.gen_window(N, W, s.vocab, seed=100 + seed)
+        ref = la.lookahead(om, MICRO_PROMPT, N, W, G, n_new, win, prompt_ref=True,
+                           temperature=T, seed=seed, pool_cap=2 * G, pool_lru=lru,
+                           pool_context=ctx)
+        ses = gm.session(MICRO_PROMPT, N, W, G, n_new, window=win, prompt_ref=True,
+                         temperature=T, seed=seed, pool_cap=2 * G, pool_lru=lru,
+                         pool_context=ctx)
+        toks = ses.decode()
+        k = _decided_prefix(ref, ses.per_step, toks)
+        if k == len(ref.margins):
+            assert toks == ref.tokens
+            st = ses.stats()
+            assert (st["inserts"], st["dup_skips"], st["evictions"]) == \
+                (ref.pool.inserts, ref.pool.dup_skips, ref.pool.evictions)
+        compared += k
+        ses.close()
+    assert compared >= 24
