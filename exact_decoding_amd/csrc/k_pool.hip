@@ -171,59 +171,90 @@ __global__ __launch_bounds__(256) void k_gather(PoolDesc pool, StepIO io, RowLay
 }
 
 constexpr int VMAX_M = 2048;  // rows staged in LDS by the verify kernel
+constexpr int VFY_T = 256;    // threads of the verify kernel (four waves)
 
-__global__ __launch_bounds__(64) void k_verify(PoolDesc pool, StepIO io, RowLayout L) {
+// Greedy verification ([LD] §3.4 "Greedy verification algorithm (Algorithm
+// 3)"), then the lookahead branch's harvest, pool insert and slide.
+//  * compare: slot u = g(N-1) + i-1 of the G x (N-1) grid says whether
+//    candidate token cand[g][i-1] equals the argmax of the row that predicts
+//    position P+i (row 0 for i = 1, else candidate g's row i-2); the slots
+//    are spread over all lanes of the four waves;
+//  * longest-prefix scan: candidate g's accepted length is the count of its
+//    leading matching slots; the best candidate is found with a max over
+//    the key (length << 11 | 2047 - g), i.e. the longest, then the first;
+//  * one thread then commits, emits and updates the counters (<= N tokens).
+// The harvest forms one n-gram per window column k, for every k < W: key
+// win[0][k], suffix win[1..N-2][k] followed by the column's new token
+// ([LD] §3.4 "N-gram harvesting and pool update").  Columns with the same
+// key go to the same bucket and must be inserted in column order (a repeat
+// within the step is a duplicate), so the lowest column of each key inserts
+// all of that key's columns in order; different keys touch different
+// buckets.  Columns are dealt to the 256 threads with a stride, so any W the
+// step allows is harvested.
+__global__ __launch_bounds__(VFY_T) void k_verify(PoolDesc pool, StepIO io, RowLayout L) {
   __shared__ int32_t a[VMAX_M];
   __shared__ int32_t cand[VMAX_M];
   __shared__ int32_t win[VMAX_M];
-  __shared__ int red[64][5];
+  __shared__ uint8_t match[VMAX_M];
+  __shared__ int s_key[VFY_T / 64];
+  __shared__ int red[VFY_T / 64][5];
   DevState* st = io.st;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int n1 = L.N - 1, W = L.W, G = L.G, M = L.M;
   const int cur_old = io.ids[0];  // the step's current token (row 0)
-  for (int i = lane; i < M; i += 64) a[i] = io.amax[i];
-  for (int i = lane; i < G * n1; i += 64) cand[i] = io.cand[i];
-  for (int i = lane; i < W * n1; i += 64) win[i] = io.win[i];
+  const int vbase = 1 + W * n1;
+  for (int i = tid; i < M; i += VFY_T) a[i] = io.amax[i];
+  for (int i = tid; i < G * n1; i += VFY_T) cand[i] = io.cand[i];
+  for (int i = tid; i < W * n1; i += VFY_T) win[i] = io.win[i];
   __syncthreads();
 
-  if (lane == 0 && io.temp <= 0.f) {
-    const int vbase = 1 + W * n1;
+  if (io.temp <= 0.f) {
     const int ncand = st->ncand;
-    int best = 0, bg = 0;
-    for (int g = 0; g < ncand; ++g) {
+    for (int u = tid; u < G * n1; u += VFY_T) {
+      const int g = u / n1, i = u - g * n1 + 1;
+      const int pred = i == 1 ? 0 : vbase + g * n1 + (i - 2);
+      match[u] = g < ncand && cand[u] == a[pred];
+    }
+    __syncthreads();
+    int key = 2047;  // nothing accepted, candidate 0
+    for (int g = tid; g < ncand; g += VFY_T) {
       int acc = 0;
-      for (int i = 1; i <= n1; ++i) {
-        const int pred = i == 1 ? 0 : vbase + g * n1 + (i - 2);
-        if (cand[g * n1 + i - 1] != a[pred]) break;
-        acc = i;
+      while (acc < n1 && match[g * n1 + acc]) ++acc;
+      key = max(key, (acc << 11) | (2047 - g));
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) key = max(key, __shfl_xor(key, o, 64));
+    if (lane == 0) s_key[wv] = key;
+    __syncthreads();
+    if (tid == 0) {
+      for (int w = 1; w < VFY_T / 64; ++w) key = max(key, s_key[w]);
+      const int best = key >> 11, bg = 2047 - (key & 2047);
+      const int bonus = best == 0 ? a[0] : a[vbase + bg * n1 + best - 1];
+      // commit: row 0 and the accepted candidate rows become cache rows P..P+best
+      st->commit_p = st->P;
+      st->commit_n = best + 1;
+      st->commit_rows[0] = 0;
+      for (int j = 1; j <= best; ++j) st->commit_rows[j] = vbase + bg * n1 + j - 1;
+      st->P += best + 1;
+      // emit, truncated to the budget; stop after EOS
+      const int room = io.max_new - st->total;
+      int n = 0, done = 0;
+      for (int j = 0; j <= best && n < room; ++j) {
+        const int tok = j < best ? cand[bg * n1 + j] : bonus;
+        st->out[n++] = tok;
+        if (io.eos >= 0 && tok == io.eos) { done = 1; break; }
       }
-      if (acc > best) { best = acc; bg = g; }
+      st->n_out = n;
+      st->total += n;
+      if (st->total >= io.max_new) done = 1;
+      if (done) st->done = 1;
+      st->cur = bonus;
+      st->stats[ST_HIST0 + best] += 1;
+      st->stats[ST_STEPS] += 1;
+      st->stats[ST_TOKENS] += n;
     }
-    const int bonus = best == 0 ? a[0] : a[vbase + bg * n1 + best - 1];
-    // commit: row 0 and the accepted candidate rows become cache rows P..P+best
-    st->commit_p = st->P;
-    st->commit_n = best + 1;
-    st->commit_rows[0] = 0;
-    for (int j = 1; j <= best; ++j) st->commit_rows[j] = vbase + bg * n1 + j - 1;
-    st->P += best + 1;
-    // emit, truncated to the budget; stop after EOS
-    const int room = io.max_new - st->total;
-    int n = 0, done = 0;
-    for (int j = 0; j <= best && n < room; ++j) {
-      const int tok = j < best ? cand[bg * n1 + j] : bonus;
-      st->out[n++] = tok;
-      if (io.eos >= 0 && tok == io.eos) { done = 1; break; }
-    }
-    st->n_out = n;
-    st->total += n;
-    if (st->total >= io.max_new) done = 1;
-    if (done) st->done = 1;
-    st->cur = bonus;
-    st->stats[ST_HIST0 + best] += 1;
-    st->stats[ST_STEPS] += 1;
-    st->stats[ST_TOKENS] += n;
   }
-  if (lane == 0) {
+  if (tid == 0) {
     // the token before the new cur: the second to last emitted, or the old
     // cur when one token was emitted (greedy above, or sampling verification
     // before this kernel); a truncated step ends the session
@@ -231,33 +262,34 @@ __global__ __launch_bounds__(64) void k_verify(PoolDesc pool, StepIO io, RowLayo
     st->prev = n >= 2 ? st->out[n - 2] : cur_old;
   }
 
-  // lookahead branch: harvest one n-gram per column (oldest level .. newest,
-  // then the column's new token) and insert in column order.  Columns sharing
-  // a first token are inserted by the lowest such column's lane, in order.
   InsertCounts c = {0, 0, 0, 0, 0};
-  if (lane < W) {
-    const int key = win[lane];
+  for (int k = tid; k < W; k += VFY_T) {
+    const int key = win[k];
     bool leader = true;
-    for (int k2 = 0; k2 < lane; ++k2)
+    for (int k2 = 0; k2 < k; ++k2)
       if (win[k2] == key) { leader = false; break; }
-    if (leader) {
-      int32_t sfx[LA_MAX_N];
-      for (int k2 = lane; k2 < W; ++k2) {
-        if (win[k2] != key) continue;
-        for (int l = 1; l < n1; ++l) sfx[l - 1] = win[l * W + k2];
-        sfx[n1 - 1] = a[1 + (n1 - 1) * W + k2];
-        // context: the level-0 token to the column's left, or the step's cur
-        pool_insert(pool, key, sfx, k2 > 0 ? win[k2 - 1] : cur_old, c);
-      }
+    if (!leader) continue;
+    int32_t sfx[LA_MAX_N];
+    for (int k2 = k; k2 < W; ++k2) {
+      if (win[k2] != key) continue;
+      for (int l = 1; l < n1; ++l) sfx[l - 1] = win[l * W + k2];
+      sfx[n1 - 1] = a[1 + (n1 - 1) * W + k2];
+      // context: the level-0 token to the column's left, or the step's cur
+      pool_insert(pool, key, sfx, k2 > 0 ? win[k2 - 1] : cur_old, c);
     }
   }
-  red[lane][0] = c.ins; red[lane][1] = c.dup; red[lane][2] = c.ev;
-  red[lane][3] = c.ngr; red[lane][4] = c.keys;
+  int cv[5] = {c.ins, c.dup, c.ev, c.ngr, c.keys};
+#pragma unroll
+  for (int j = 0; j < 5; ++j) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) cv[j] += __shfl_xor(cv[j], o, 64);
+    if (lane == 0) red[wv][j] = cv[j];
+  }
   __syncthreads();
-  if (lane == 0) {
+  if (tid == 0) {
     long long t[5] = {0, 0, 0, 0, 0};
-    for (int i = 0; i < 64; ++i)
-      for (int j = 0; j < 5; ++j) t[j] += red[i][j];
+    for (int w = 0; w < VFY_T / 64; ++w)
+      for (int j = 0; j < 5; ++j) t[j] += red[w][j];
     st->stats[ST_INSERTS] += t[0];
     st->stats[ST_DUPS] += t[1];
     st->stats[ST_EVICT] += t[2];
@@ -265,7 +297,7 @@ __global__ __launch_bounds__(64) void k_verify(PoolDesc pool, StepIO io, RowLayo
     st->stats[ST_KEYS] += t[4];
   }
   // slide: drop the oldest level, the new tokens become the newest level
-  for (int u = lane; u < W * n1; u += 64) {
+  for (int u = tid; u < W * n1; u += VFY_T) {
     const int l = u / W, k = u - l * W;
     io.win[u] = l + 1 < n1 ? win[(l + 1) * W + k] : a[1 + (n1 - 1) * W + k];
   }
@@ -722,8 +754,8 @@ hipError_t launch_gather(const PoolDesc& pool, const StepIO& io, const RowLayout
 
 hipError_t launch_verify(const PoolDesc& pool, const StepIO& io, const RowLayout& lay,
                          hipStream_t st) {
-  if (lay.M > VMAX_M) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_verify, dim3(1), dim3(64), 0, st, pool, io, lay);
+  if (lay.M > VMAX_M || lay.G > 1024) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_verify, dim3(1), dim3(VFY_T), 0, st, pool, io, lay);
   return hipGetLastError();
 }
 

@@ -789,11 +789,13 @@ int la_debug_logits(const la_session* s, float* out, int32_t rows) {
 
 size_t la_kernel_attention_ws_bytes(int32_t ld_ctx, int32_t H, int32_t hd, int32_t N, int32_t W,
                                     int32_t G, int32_t dtype) {
-  if (ld_ctx < 0 || H < 1 || N < 2 || W < 0 || G < 0) return 0;
+  if (ld_ctx < 0 || H < 1 || N < 2 || N > LA_MAX_N || W < 0 || G < 0) return 0;
   if (!attn_uses_mfma(dtype, hd)) return 0;
-  const int M = 1 + (W + G) * (N - 1);
+  // widen before adding: W + G may not fit an int
+  const long long M = 1 + ((long long)W + G) * (N - 1);
+  if (M < 1 || M > 2048) return 0;
   const int nsplit = attn_nchunks(ld_ctx);
-  return attn_part_floats(nsplit > 0 ? nsplit : 1, M, H, hd) * 4;
+  return attn_part_floats(nsplit > 0 ? nsplit : 1, (int)M, H, hd) * 4;
 }
 
 int la_kernel_attention(const void* q, const void* k_cache, const void* v_cache, int32_t P,
@@ -807,8 +809,8 @@ int la_kernel_attention(const void* q, const void* k_cache, const void* v_cache,
   if (hd != 16 && hd != 32 && hd != 64 && hd != 128) return fail(LA_EINVAL, "bad head_dim");
   if (N < 2 || N > LA_MAX_N || W < 0 || G < 0) return fail(LA_EINVAL, "bad N, W, G");
   if (dtype != LA_F32 && dtype != LA_BF16) return fail(LA_EINVAL, "bad dtype");
-  const long long M = 1 + (long long)(W + G) * (N - 1);
-  if (M > 2048) return fail(LA_EINVAL, "M too large");
+  const long long M = 1 + ((long long)W + G) * (N - 1);
+  if (M < 1 || M > 2048) return fail(LA_EINVAL, "1 + (W+G)(N-1) must be in [1, 2048]");
   AttnDesc a{};
   a.q = q; a.kc = k_cache ? k_cache : k_blk; a.vc = v_cache ? v_cache : v_blk;
   a.kb = k_blk; a.vb = v_blk; a.out = out;

@@ -264,15 +264,17 @@ const char* la_last_error(void);
  *   k_cache, v_cache [Hkv][ld_ctx][hd]  device, dtype; positions [0, P) used
  *   k_blk, v_blk     [M][Hkv*hd]        device, dtype
  *   out     [M][H*hd]          device, dtype (written)
- * with M = 1 + (W+G)(N-1).  Row positions are P + offset (row layout of
- * la_step).  ws: device scratch of ws_bytes >= la_kernel_attention_ws_bytes.
+ * with M = 1 + (W+G)(N-1), formed in 64-bit arithmetic; LA_EINVAL unless
+ * 1 <= M <= 2048.  Row positions are P + offset (row layout of la_step).
+ * ws: device scratch of ws_bytes >= la_kernel_attention_ws_bytes.
  * Enqueued on `hip_stream`; does not synchronise. */
 int la_kernel_attention(const void* q, const void* k_cache, const void* v_cache, int32_t P,
                         int32_t ld_ctx, const void* k_blk, const void* v_blk, void* out,
                         int32_t H, int32_t Hkv, int32_t hd, int32_t N, int32_t W, int32_t G,
                         int32_t dtype, void* ws, size_t ws_bytes, void* hip_stream);
 /* Device scratch bytes la_kernel_attention needs (partial softmax states of
- * the committed-prefix chunks); 0 when it needs none. */
+ * the committed-prefix chunks); 0 when it needs none or when the arguments
+ * are out of range (1 + (W+G)(N-1) outside [1, 2048], N outside [2, 16]). */
 size_t la_kernel_attention_ws_bytes(int32_t ld_ctx, int32_t H, int32_t hd, int32_t N, int32_t W,
                                     int32_t G, int32_t dtype);
 

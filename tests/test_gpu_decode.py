@@ -177,6 +177,40 @@ def test_tiny_edge_configs_match_oracle(tiny, N, W, G, plen, prompt_ref):
     ses.close()
 
 
+@pytest.mark.parametrize("N,W,G", [(3, 70, 4), (4, 130, 6)])
+def test_tiny_wide_window_pool_matches_oracle(tiny, N, W, G):
+    """Windows wider than one wavefront (W > 64): every window column is
+    harvested, whatever its place, so tokens, steps, the accepted-length
+    histogram and every pool counter equal the oracle's; each step makes
+    exactly W insert attempts (inserts + duplicates = prompt n-grams +
+    W * steps)."""
+    s, w, gm, om = tiny
+    n_new = 24
+    prompt = synth.prompt_motif(s.vocab, seed=1)
+    win = synth.gen_window(N, W, s.vocab, seed=2)
+    # columns past the first 64 whose key appears in none of the first 64:
+    # their n-grams reach the pool only if those columns are harvested
+    level0 = [int(t) for t in win[:W]]  # level-major: level 0 is the first W tokens
+    wide_only = set(level0[64:]) - set(level0[:64])
+    assert wide_only
+    print(f"tiny fp32 wide window N={N} W={W} G={G}", flush=True)
+    ref = la.lookahead(om, prompt, N, W, G, n_new, win, prompt_ref=True)
+    assert ref.tokens == la.greedy_ar(om, prompt, n_new).tokens
+    ses = gm.session(prompt, N, W, G, n_new, window=win, prompt_ref=True)
+    ses.decode()
+    st = ses.stats()
+    ses.close()
+    assert ses.tokens == ref.tokens
+    assert ses.per_step == ref.emitted
+    assert st["steps"] == ref.steps
+    assert [st["accept_hist"][j] for j in range(N)] == [ref.accepted.count(j) for j in range(N)]
+    assert st["inserts"] == ref.pool.inserts and st["dup_skips"] == ref.pool.dup_skips
+    assert st["evictions"] == ref.pool.evictions
+    assert st["pool_ngrams"] == ref.pool.n_ngrams() and st["pool_keys_nonempty"] == ref.pool.n_keys()
+    n_prompt_ngrams = max(0, len(prompt) - N + 1)
+    assert st["inserts"] + st["dup_skips"] == n_prompt_ngrams + W * st["steps"]
+
+
 def test_context_full_is_reported(tiny):
     """A step that would write past max_ctx is refused with LA_ECTX before any
     device work; the tokens emitted until then are the AR stream's prefix."""
@@ -207,7 +241,14 @@ def test_bf16_near_maximum_rows_bit_exact():
                         prompt_ref=True)
     assert la_ses.rows == 1981
     la_toks = la_ses.decode()
+    st = la_ses.stats()
     la_ses.close()
+    # pool invariants at 66 columns: W insert attempts per step after the
+    # prompt's n-grams; the pool holds what was inserted less what was evicted
+    n_prompt_ngrams = max(0, len(prompt) - N + 1)
+    assert st["inserts"] + st["dup_skips"] == n_prompt_ngrams + W * st["steps"]
+    assert st["pool_ngrams"] == st["inserts"] - st["evictions"]
+    assert 1 <= st["pool_keys_nonempty"] <= st["pool_ngrams"]
     ar_ses = gm.session(prompt, N, W, G, n_new, ar=True)
     ar_toks = ar_ses.decode()
     ar_ses.close()

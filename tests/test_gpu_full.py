@@ -13,15 +13,21 @@ For each model:
     (plus the float32 accumulation bound), with at most 1% of elements off
     the correctly rounded value.  float32 tensors (residual stream, logits)
     must agree to float32 accumulation accuracy.
-  * end to end, teacher-forced logits of an AR run are compared with the
-    oracle's.  At these widths the bf16 rounding noise makes any two exact
-    evaluations drift apart by more than 2e-2 over the depth of the model,
-    so the bound is a multiple of the drift between the oracle's own float64
-    and float32-accumulation evaluations of the same sequence; and every
-    token whose oracle top-2 margin exceeds twice the observed logit error
-    equals the oracle's argmax.
-The oracle runs on a short prompt prefix (its cost grows with the prefix
-length), at the full layer count and width.
+  * end to end, the logits of every step of an AR run (64 generated tokens
+    at 7B and 70B, 32 at 13B) are compared with the oracle's teacher-forced
+    logits of the same sequence.  At these widths the bf16 rounding noise
+    makes any two exact evaluations drift apart by more than the stated
+    2e-2 over the depth of the model (that bar is not met here; see the
+    precision reading of the oracle), so the tolerance is tied to the
+    oracle alone: TOL_FACTOR times the drift between the oracle's own
+    float64 and float32-accumulation evaluations of the same sequence.  The
+    GPU's error must stay within it, and at every position whose oracle
+    top-2 margin exceeds twice the tolerance (a set fixed by the oracle,
+    whatever the GPU's error) the GPU token equals the oracle's argmax; at
+    least MIN_DECIDED such positions are required per shape.
+The 13B and 70B oracle runs use a prefix of the workload's prompt (the
+oracle's cost grows with the sequence length), at the full layer count and
+width.
 """
 import numpy as np
 import pytest
@@ -38,7 +44,7 @@ from oracle.model import OracleModel, bf16_round, decode_bf16
 from progress import log as _log, ticker
 
 pytestmark = pytest.mark.gpu
-DRIFT_FACTOR = 4.0
+TOL_FACTOR = 1.5
 
 
 def _build(name):
@@ -61,8 +67,11 @@ def _ar_logits(gm, prompt, n, N):
     return toks, np.array(lg)
 
 
-def _oracle_check(s, w, gm, prompt, n_new, N):
+def _oracle_check(s, w, gm, prompt, n_new, N, min_decided):
+    """GPU AR logits at every generated position against the oracle's
+    teacher-forced logits of the GPU's own token stream (see module doc)."""
     toks, lg = _ar_logits(gm, prompt, n_new, N)
+    assert len(toks) == n_new and lg.shape == (n_new, s.vocab)
     om = OracleModel(s, w)
     om.keep = False
     om.on_layer = ticker(s.name)
@@ -73,14 +82,19 @@ def _oracle_check(s, w, gm, prompt, n_new, N):
     _log(f"{s.name}: the same with float32 accumulation")
     ref32 = la.score(om, seq)[len(prompt) - 1:]
     drift = np.abs(ref32 - ref).max()
+    tol = TOL_FACTOR * drift
     err = np.abs(lg - ref).max()
     srt = np.sort(ref, axis=1)
     margin = srt[:, -1] - srt[:, -2]
-    sure = margin > 2 * err
-    _log(f"{s.name}: max |logit diff| GPU {err:.3e}, oracle f32-vs-f64 drift {drift:.3e}; "
-         f"{int(sure.sum())}/{len(sure)} positions decided")
-    assert err <= DRIFT_FACTOR * drift
-    assert np.array_equal(np.array(toks)[sure], np.argmax(ref, axis=1)[sure])
+    sure = margin > 2 * tol
+    agree = np.array(toks)[sure] == np.argmax(ref, axis=1)[sure]
+    _log(f"{s.name}: {n_new} tokens scored; max |logit diff| GPU {err:.3e} (bar 2e-2 not met "
+         f"at this width), oracle f32-vs-f64 drift {drift:.3e}, tolerance {tol:.3e}; "
+         f"{int(sure.sum())}/{len(sure)} positions decided (margin > {2 * tol:.3e}, minimum "
+         f"{min_decided}), {int(agree.sum())} agree")
+    assert err <= tol
+    assert int(sure.sum()) >= min_decided
+    assert agree.all()
 
 
 def _bf16_close(name, gpu_bits, ref, bf16, max_frac=0.01):
@@ -196,7 +210,7 @@ def test_llama7b_full():
     prompt = synth.prompt_zipf_spans(s.vocab, length=128, seed=1)
     _bit_exact(gm, prompt, 5, 15, 15, 256, s.vocab)
     _layer_check(s, w, gm, prompt, 5, 15, 15, range(s.n_layers))
-    _oracle_check(s, w, gm, prompt, 4, 5)
+    _oracle_check(s, w, gm, prompt, 64, 5, min_decided=8)
     gm.close()
 
 
@@ -205,7 +219,7 @@ def test_codellama13b_full():
     prompt = synth.prompt_code_lines(s.vocab, length=512, seed=1)
     _bit_exact(gm, prompt, 5, 15, 15, 512, s.vocab)
     _layer_check(s, w, gm, prompt, 5, 15, 15, [0, 1, s.n_layers // 2, s.n_layers - 1])
-    _oracle_check(s, w, gm, prompt[:48], 3, 5)
+    _oracle_check(s, w, gm, prompt[:128], 32, 5, min_decided=3)
     gm.close()
 
 
@@ -214,7 +228,7 @@ def test_llama70b_full():
     prompt = synth.prompt_zipf_spans(s.vocab, length=1024, seed=1)
     _bit_exact(gm, prompt, 5, 7, 7, 256, s.vocab)
     _layer_check(s, w, gm, prompt, 5, 7, 7, [0, 1, s.n_layers // 2, s.n_layers - 1])
-    _oracle_check(s, w, gm, prompt[:16], 2, 5)
+    _oracle_check(s, w, gm, prompt[:32], 64, 5, min_decided=1)
     gm.close()
 
 

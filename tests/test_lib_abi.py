@@ -147,6 +147,12 @@ def test_kernel_hooks_validate():
     # bf16 head_dim 128 needs the partial-state scratch
     assert B.la_kernel_attention_ws_bytes(512, 32, 128, 5, 15, 15, B.LA_BF16) > 0
     assert lib.la_kernel_attention(P, P, P, 4, 8, P, P, P, 4, 4, 128, 3, 2, 2, 1, None, 0, None) == B.LA_ENOMEM
+    # W + G past INT_MAX: widened before the row count is formed, then refused
+    imax = 2**31 - 1
+    assert lib.la_kernel_attention(P, P, P, 4, 8, P, P, P, 4, 4, 128, 3, imax, 2, 1, None, 0, None) == B.LA_EINVAL
+    assert lib.la_kernel_attention(P, P, P, 4, 8, P, P, P, 4, 4, 128, 3, imax, imax, 1, None, 0, None) == B.LA_EINVAL
+    assert B.la_kernel_attention_ws_bytes(512, 32, 128, 3, imax, 2, B.LA_BF16) == 0
+    assert B.la_kernel_attention_ws_bytes(512, 32, 128, 3, imax, imax, B.LA_BF16) == 0
     # bf16 GEMM needs K % 64 == 0
     assert lib.la_kernel_gemm(P, 4, 100, P, 64, P, B.LA_BF16, None, 0, None) == B.LA_EINVAL
     assert B.la_kernel_gemm_ws_bytes(121, 4096, 4096) > 0
