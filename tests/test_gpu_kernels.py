@@ -155,7 +155,8 @@ def test_attention_matches_oracle(P, H, Hkv, hd, N, W, G, dtype):
 
 
 @pytest.mark.parametrize("P,W,G", [(5, 3, 3), (63, 3, 3), (64, 3, 3), (130, 3, 3), (300, 3, 3),
-                                   (1100, 3, 3), (130, 15, 15), (300, 15, 15), (1100, 15, 15)])
+                                   (525, 3, 3), (1100, 3, 3), (130, 15, 15), (300, 15, 15),
+                                   (525, 15, 15), (1100, 15, 15)])
 def test_attention_verification_row_equals_ar_query(P, W, G):
     """Verification row (g, i) == one query at P+i over a cache holding the
     prefix and the row's chain (what an autoregressive step computes).
@@ -189,4 +190,5 @@ def test_attention_verification_row_equals_ar_query(P, W, G):
                               B.LA_BF16, ws, None)
         torch.cuda.synchronize()
         assert torch.equal(out1[0], out[r]), (r, g, i)
+
 
