@@ -19,6 +19,7 @@ LA_EINVAL, LA_ENOMEM, LA_ECTX, LA_EHIP, LA_ESTATE = -1, -2, -3, -4, -5
 LA_F32, LA_BF16 = 0, 1
 LA_MAX_N = 16
 LA_PROBE_BLOCKS = 2048
+LA_NOALLOC_SCRATCH_BYTES = 32 << 20
 LA_PROMPT_REF, LA_AR, LA_NO_GRAPH, LA_POOL_LRU, LA_POOL_CONTEXT = 1, 2, 8, 16, 32
 
 EXPORTS = [
@@ -26,7 +27,7 @@ EXPORTS = [
     "la_pool_stats", "la_debug_logits", "la_session_rows", "la_session_free", "la_last_error",
     "la_kernel_attention", "la_kernel_gemm", "la_kernel_gemm_ws_bytes", "la_step_profile",
     "la_kernel_attention_ws_bytes", "la_packed_bytes", "la_pack_weight", "la_probe_read",
-    "la_step_trace", "la_step_trace_bytes", "la_philox_uniform",
+    "la_step_trace", "la_step_trace_bytes", "la_philox_uniform", "la_kernel_gemm_noalloc",
 ]
 
 PROF_KINDS = ["gemm", "lm_head", "attention", "norm", "epilogue", "argmax", "bookkeeping"]
@@ -115,6 +116,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.la_kernel_attention_ws_bytes.argtypes = [I32, I32, I32, I32, I32, I32, I32]
     lib.la_kernel_attention_ws_bytes.restype = SZ
     lib.la_kernel_gemm.argtypes = [P, I32, I32, P, I32, P, I32, P, SZ, P]
+    lib.la_kernel_gemm_noalloc.argtypes = [P, I32, I32, P, I32, P, I32, P]
     lib.la_probe_read.argtypes = [P, SZ, P, P]
     lib.la_philox_uniform.argtypes = [ctypes.c_uint64, ctypes.c_uint64, I32, P, P]
     lib.la_packed_bytes.argtypes = [I32, I32]
@@ -278,3 +280,8 @@ def la_kernel_gemm(x, M, K, w, N, y, dtype, ws, stream) -> None:
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib.la_kernel_gemm(_ptr(x), M, K, _ptr(w), N, _ptr(y), dtype, _ptr(ws), nbytes,
                               ctypes.c_void_p(_stream_handle(stream))))
+
+
+def la_kernel_gemm_noalloc(x, M, K, w, N, y, dtype, stream) -> None:
+    _check(load_library().la_kernel_gemm_noalloc(_ptr(x), M, K, _ptr(w), N, _ptr(y), dtype,
+                                                 ctypes.c_void_p(_stream_handle(stream))))

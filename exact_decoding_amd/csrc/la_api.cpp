@@ -11,6 +11,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -49,6 +50,35 @@ struct LayerW {
 size_t dtype_size(int dt) { return dt == LA_BF16 ? 2 : 4; }
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Scratch of la_kernel_gemm_noalloc: one copy in every GPU's memory for the
+// life of the process.  Host code never uses the array's name as an address
+// (on the host it is a stand-in, not device memory): it takes the device
+// address that hipGetSymbolAddress returns, once per device, with that
+// device current.
+static __device__ __align__(256) char scratch[LA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of the current device's scratch array.
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(LA_EHIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(LA_EHIP, "device index out of range");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(LA_EHIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return LA_OK;
+}
 
 }  // namespace
 
@@ -860,6 +890,26 @@ size_t la_kernel_gemm_ws_bytes(int32_t M, int32_t K, int32_t N) {
   if (M < 1 || K < 1 || N < 1) return 0;
   const SplitPlan sp = gemm_plan(N, K, LA_BF16);
   return sp.np > 1 ? (size_t)sp.np * M * N * 4 : 0;
+}
+
+int la_kernel_gemm_noalloc(const void* x, int32_t M, int32_t K, const void* w, int32_t N, float* y,
+                           int32_t dtype, void* hip_stream) {
+  if (!x || !w || !y) return fail(LA_EINVAL, "null pointer");
+  if (M < 1 || K < 1 || N < 1) return fail(LA_EINVAL, "sizes must be >= 1");
+  if (dtype != LA_F32 && dtype != LA_BF16) return fail(LA_EINVAL, "bad dtype");
+  if (dtype == LA_BF16 && K % 64) return fail(LA_EINVAL, "bf16 needs K % 64 == 0");
+  const SplitPlan sp = gemm_plan(N, K, dtype);
+  const size_t need = sp.np > 1 ? (size_t)sp.np * M * N * 4 : 0;
+  if (need > (size_t)LA_NOALLOC_SCRATCH_BYTES)
+    return fail(LA_ENOMEM, "partial sums need " + std::to_string(need) +
+                               " bytes, beyond the static scratch of " +
+                               std::to_string(LA_NOALLOC_SCRATCH_BYTES));
+  void* ws = nullptr;
+  if (need) {
+    const int rc = scratch_address(&ws);
+    if (rc != LA_OK) return rc;
+  }
+  return la_kernel_gemm(x, M, K, w, N, y, dtype, ws, need, hip_stream);
 }
 
 int la_kernel_gemm(const void* x, int32_t M, int32_t K, const void* w, int32_t N, float* y,

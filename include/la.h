@@ -289,6 +289,23 @@ int la_kernel_gemm(const void* x, int32_t M, int32_t K, const void* w, int32_t N
                    int32_t dtype, void* ws, size_t ws_bytes, void* hip_stream);
 size_t la_kernel_gemm_ws_bytes(int32_t M, int32_t K, int32_t N);
 
+/* la_kernel_gemm for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same product, split and summation order, so y is bit-identical to
+ * la_kernel_gemm's, but its partial sums live in a scratch array the library
+ * holds in every GPU's memory for the life of the process
+ * (LA_NOALLOC_SCRATCH_BYTES per GPU).  It allocates nothing: no hipMalloc,
+ * hipFree or allocating library call; the caller passes x, w and y as for
+ * la_kernel_gemm.  LA_ENOMEM when la_kernel_gemm_ws_bytes(M, K, N) exceeds
+ * LA_NOALLOC_SCRATCH_BYTES; LA_EINVAL on bad arguments; LA_EHIP when the
+ * scratch array cannot be located on the current device.  Every call on one
+ * GPU uses that GPU's array: calls that overlap on one GPU (other streams,
+ * other host threads) race and must be serialised by the caller.  The array
+ * keeps the last call's partial sums.  Enqueued on `hip_stream`. */
+#define LA_NOALLOC_SCRATCH_BYTES 33554432
+int la_kernel_gemm_noalloc(const void* x, int32_t M, int32_t K, const void* w, int32_t N, float* y,
+                           int32_t dtype, void* hip_stream);
+
 /* The draws of sampling verification (test hook): out[i] = draw i of step
  * `step` under `seed`, i < n: word 0 of Philox4x32-10 (Salmon et al., "Parallel
  * Random Numbers: As Easy as 1, 2, 3", SC 2011) at counter (step mod 2^32,

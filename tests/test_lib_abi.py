@@ -156,6 +156,14 @@ def test_kernel_hooks_validate():
     # bf16 GEMM needs K % 64 == 0
     assert lib.la_kernel_gemm(P, 4, 100, P, 64, P, B.LA_BF16, None, 0, None) == B.LA_EINVAL
     assert B.la_kernel_gemm_ws_bytes(121, 4096, 4096) > 0
+    # the allocation-free variant: same argument checks, and partial sums
+    # beyond its static scratch are refused before any device work
+    assert lib.la_kernel_gemm_noalloc(None, 4, 64, P, 64, P, B.LA_BF16, None) == B.LA_EINVAL
+    assert lib.la_kernel_gemm_noalloc(P, 4, 100, P, 64, P, B.LA_BF16, None) == B.LA_EINVAL
+    assert lib.la_kernel_gemm_noalloc(P, 0, 64, P, 64, P, B.LA_BF16, None) == B.LA_EINVAL
+    assert B.la_kernel_gemm_ws_bytes(2048, 4096, 4096) > B.LA_NOALLOC_SCRATCH_BYTES
+    assert lib.la_kernel_gemm_noalloc(P, 2048, 4096, P, 4096, P, B.LA_BF16, None) == B.LA_ENOMEM
+    assert b"static scratch" in lib.la_last_error()
 
 
 def test_binding_constants_match_header():
