@@ -68,6 +68,10 @@ def parse():
                     help="instead of the benchmark line: step time against the row count "
                          "M over a grid of (N, W = G), one JSON line per configuration")
     ap.add_argument("--sweep-steps", type=int, default=32)
+    ap.add_argument("--scaling-fit", action="store_true",
+                    help="step compression S of the small random-init models over N and W = G "
+                         "through the C-ABI, checked against the oracle's values in "
+                         "tests/golden/scaling_points.json, and the Eq. 5/7 fit of (alpha, f)")
     ap.add_argument("--attention", action="store_true",
                     help="instead: time the lookahead attention call alone (32 heads, head_dim 128, "
                          "bf16) at prefixes 512, 2048, 8192 for (N, W, G) = (5, 15, 15) and (7, 7, 7)")
@@ -186,6 +190,12 @@ def cpu_baseline(shape, weights, prompt, n_tokens):
 
 SWEEP_N = (3, 5, 7)
 SWEEP_W = (1, 2, 4, 7, 10, 15, 20, 30)
+# [LD] Table 3 (LLaMA-2-7B-Chat, MT-Bench, one A100): label, N, W, G, prompt as
+# reference, the S and the speedup the pages report
+TABLE3 = [("3", 10, 1, 3, True, 1.45, 1.36), ("4", 5, 1, 10, True, 1.51, 1.36),
+          ("5", 5, 1, 30, False, 1.12, 1.04), ("6", 5, 1, 30, True, 1.59, 1.46),
+          ("7", 5, 30, 1, False, 1.79, 1.61), ("8", 5, 15, 15, False, 1.96, 1.78),
+          ("9", 5, 15, 15, True, 2.05, 1.88)]
 
 
 def sweep(args, model, shape, prompt):
@@ -195,10 +205,10 @@ def sweep(args, model, shape, prompt):
     import synth
     K = args.sweep_steps
 
-    def time_steps(N, W, G, ar):
+    def time_steps(N, W, G, ar, prompt_ref=True):
         ses = model.session(prompt, N, W, G, K + 8, ar=ar,
                             window=None if ar else synth.gen_window(N, W, shape.vocab, seed=2),
-                            prompt_ref=not ar)
+                            prompt_ref=prompt_ref and not ar)
         for _ in range(4):
             ses.step()
         n0, s0 = len(ses.tokens), len(ses.per_step)
@@ -237,6 +247,17 @@ def sweep(args, model, shape, prompt):
     best = planner.best_config(table, ar_ms)
     print(json.dumps({"shape": shape.name, "best_under_pages_model": best,
                       "alpha": planner.PAGES_ALPHA, "f": planner.PAGES_F}), flush=True)
+    # the pages' ablation configurations (Table 3 ③-⑨, several with G != W):
+    # the step each costs here and, with the S the pages measured for it,
+    # the speedup it would give on this GPU
+    for label, N, W, G, ref, S_pages, sp_pages in TABLE3:
+        ms, S, rows = time_steps(N, W, G, False, prompt_ref=ref)
+        print(json.dumps({"shape": shape.name, "table3": label, "N": N, "W": W, "G": G,
+                          "prompt_ref": ref, "M": rows, "step_ms": ms, "ar_step_ms": ar_ms,
+                          "break_even_S": ms / ar_ms, "measured_S": S, "pages_S": S_pages,
+                          "pages_speedup_A100": sp_pages,
+                          "speedup_here_at_pages_S": S_pages * ar_ms / ms}), flush=True)
+    return {"rows": table, "ar_ms": ar_ms}
 
 
 def attention_bench(read_gbps):
@@ -339,6 +360,51 @@ def gemm_bench(shape, rows, read_gbps, reps=10):
         torch.cuda.empty_cache()
 
 
+def scaling_fit(sweep_table=None):
+    """[LD] §4 "Scaling Law": S = tokens / steps measured through the C-ABI
+    on the small random-init models that repeat n-grams, for the (N, W = G)
+    grid of tests/golden/scaling_points.json; every S must equal the
+    oracle's value there (the fp32 engine reproduces the oracle's steps);
+    then (alpha, f) of Eq. 5/7 fitted per model, its residual, and the
+    configuration the fitted model favours on the measured 7B step times."""
+    import synth
+    from exact_decoding_amd import planner
+    from exact_decoding_amd.runtime import Model
+    gold = json.load(open(os.path.join(ROOT, "tests", "golden", "scaling_points.json")))
+    rec = gold["recipe"]
+    fits = {}
+    for name, pts in gold["models"].items():
+        s = synth.SHAPES[name]
+        model = Model(s, synth.gen_weights(s, 0))
+        prompts = [synth.prompt_motif(s.vocab, seed=k) for k in range(rec["prompts"])]
+        trip, equal = [], True
+        for p in pts:
+            N, W, G = p["N"], p["W"], p["G"]
+            win = synth.gen_window(N, W, s.vocab, seed=2)
+            toks = steps = 0
+            for pr in prompts:
+                ses = model.session(pr, N, W, G, rec["new_tokens"], window=win, prompt_ref=True)
+                toks += len(ses.decode())
+                steps += ses.stats()["steps"]
+                ses.close()
+            equal = equal and toks == p["tokens"] and steps == p["steps"]
+            trip.append((N, W, toks / steps))
+        model.close()
+        alpha, f = planner.fit(trip)
+        res = [planner.compression(alpha, n, w, f) - S for n, w, S in trip]
+        rms = (sum(r * r for r in res) / len(res)) ** 0.5
+        fits[name] = (alpha, f)
+        out = {"study": "scaling-law fit", "shape": name, "points": len(trip),
+               "equal_to_oracle": equal, "alpha": alpha, "f": f, "rms_residual": rms,
+               "max_residual": max(abs(r) for r in res),
+               "S": [[n, w, round(S, 4)] for n, w, S in trip]}
+        if sweep_table:
+            out["best_on_7b_steps"] = planner.best_config(sweep_table["rows"], sweep_table["ar_ms"],
+                                                          alpha, f)
+        print(json.dumps(out), flush=True)
+    return fits
+
+
 def pool_study(N=4, W=5, G=5, n_new=128, seeds=8):
     """S = tokens / steps of whole generations against the pool cap, its
     eviction policy and the candidate selection rule (the newest G, or by
@@ -433,6 +499,9 @@ def main():
     if args.pool_study:
         pool_study()
         return
+    if args.scaling_fit and not args.sweep:
+        scaling_fit()
+        return
     t0 = time.time()
     log(f"[bench] generating + uploading {shape.name} weights")
     weights_np = []
@@ -454,7 +523,10 @@ def main():
     window = synth.gen_window(N, W, shape.vocab, seed=2)
     graph = not args.no_graph
     if args.sweep:
-        sweep(args, model, shape, prompt)
+        table = sweep(args, model, shape, prompt)
+        if args.scaling_fit:
+            model.close()
+            scaling_fit(table)
         return
     sync = torch.cuda.synchronize
 
@@ -505,6 +577,28 @@ def main():
     ar_tps = toks_ar / dt_ar
     log(f"[bench] autoregressive: {toks_ar} tokens in {dt_ar:.3f}s -> {ar_tps:.1f} tok/s, "
         f"{dt_ar * 1e3 / ar_steps:.3f} ms/step")
+
+    # the same configuration with LA_ADAPTIVE_G: each step computes candidate
+    # rows only as far as its candidates need (every token, step and pool
+    # counter as with the fixed width)
+    adaptive = None
+    if args.temperature == 0:
+        def la_adaptive():
+            return model.session(prompt, N, W, G, args.max_new, window=window, prompt_ref=True,
+                                 graph=graph, pool_cap=args.pool_cap, pool_lru=args.pool_lru,
+                                 adaptive_g=True)
+        ses = la_adaptive()
+        toks_a = ses.decode()
+        st_a = ses.stats()
+        ses.close()
+        dt_a, toks_ad = timed_steps(lambda: [la_adaptive() for _ in range(n_sess)], args.steps, sync)
+        adaptive = {"tokens_per_s": toks_ad / dt_a, "ms_per_step": dt_a * 1e3 / args.steps,
+                    "rows_per_step_mean": st_a["rows_total"] / st_a["steps"],
+                    "rows_per_step_max": 1 + (W + G) * (N - 1),
+                    "equals_fixed_width": toks_a == la_tokens_ref and st_a["steps"] == gen_steps,
+                    "speedup_vs_ar": (toks_ad / dt_a) / ar_tps}
+        log(f"[bench] adaptive G: {toks_ad} tokens in {dt_a:.3f}s -> {toks_ad / dt_a:.1f} tok/s, "
+            f"{dt_a * 1e3 / args.steps:.3f} ms/step, {adaptive['rows_per_step_mean']:.1f} rows/step")
 
     # exactness spot check: the lookahead stream equals the AR stream
     ses = ar_session()
@@ -606,6 +700,7 @@ def main():
         "ar_tokens_per_s": ar_tps,
         "speedup_vs_ar": la_tps / ar_tps,
         "lookahead_equals_ar": exact,
+        "adaptive_G": adaptive,
         "step_hbm": {"bytes_per_step": step_bytes, "GBps": step_gbps, "frac": step_gbps / HBM_PEAK_GBPS,
                      "frac_of_achievable": step_gbps / read_gbps if read_gbps else None,
                      "P_avg": P_avg},

@@ -21,6 +21,7 @@ LA_MAX_N = 16
 LA_PROBE_BLOCKS = 2048
 LA_NOALLOC_SCRATCH_BYTES = 32 << 20
 LA_PROMPT_REF, LA_AR, LA_NO_GRAPH, LA_POOL_LRU, LA_POOL_CONTEXT = 1, 2, 8, 16, 32
+LA_ADAPTIVE_G = 64
 
 EXPORTS = [
     "la_model_load", "la_model_free", "la_session_bytes", "la_prefill", "la_step",
@@ -62,7 +63,7 @@ class PoolStats(ctypes.Structure):
                 ("pool_ngrams", ctypes.c_int64), ("pool_keys_nonempty", ctypes.c_int64),
                 ("inserts", ctypes.c_int64), ("dup_skips", ctypes.c_int64),
                 ("evictions", ctypes.c_int64), ("gathers_nonempty", ctypes.c_int64),
-                ("cand_total", ctypes.c_int64)]
+                ("cand_total", ctypes.c_int64), ("rows_total", ctypes.c_int64)]
 
     def as_dict(self) -> dict:
         d = {f: getattr(self, f) for f, _ in self._fields_ if f != "accept_hist"}

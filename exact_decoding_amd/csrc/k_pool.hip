@@ -295,6 +295,10 @@ __global__ __launch_bounds__(VFY_T) void k_verify(PoolDesc pool, StepIO io, RowL
     st->stats[ST_EVICT] += t[2];
     st->stats[ST_NGRAMS] += t[3];
     st->stats[ST_KEYS] += t[4];
+    // candidates the next step's gather will take for the new cur (every
+    // insert of this step is done: they precede the barrier above)
+    const int nc = io.gmax > 0 ? pool.cnt[st->cur] : 0;
+    st->next_g = nc < io.gmax ? nc : io.gmax;
   }
   // slide: drop the oldest level, the new tokens become the newest level
   for (int u = tid; u < W * n1; u += VFY_T) {

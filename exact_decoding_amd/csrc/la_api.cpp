@@ -209,7 +209,9 @@ int check_params(const la_model* m, const la_decode_params* p) {
   if (p->max_ctx < 2) return fail(LA_EINVAL, "max_ctx must be >= 2");
   if (p->max_new < 1) return fail(LA_EINVAL, "max_new must be >= 1");
   if (p->eos_id >= m->d.vocab) return fail(LA_EINVAL, "eos_id out of range");
-  if (p->flags & ~(LA_PROMPT_REF | LA_AR | LA_NO_GRAPH | LA_POOL_LRU | LA_POOL_CONTEXT)) return fail(LA_EINVAL, "unknown flags");
+  if (p->flags & ~(LA_PROMPT_REF | LA_AR | LA_NO_GRAPH | LA_POOL_LRU | LA_POOL_CONTEXT |
+                   LA_ADAPTIVE_G))
+    return fail(LA_EINVAL, "unknown flags");
   const long long W = ar ? 0 : p->W, G = ar ? 0 : p->G;
   const long long M = 1 + (W + G) * (p->N - 1);
   if (M > 2048) return fail(LA_EINVAL, "1 + (W+G)(N-1) must be <= 2048");
@@ -232,9 +234,12 @@ struct la_session {
   Views v{};
   char* base = nullptr;
   hipStream_t stream = nullptr;
-  RowLayout lay{};
-  hipGraph_t graph = nullptr;
-  hipGraphExec_t exec = nullptr;
+  RowLayout lay{};  // layout of the step being enqueued
+  // captured steps, one per verification width G' (all G' = G without
+  // LA_ADAPTIVE_G)
+  std::vector<hipGraph_t> graphs;
+  std::vector<hipGraphExec_t> execs;
+  long long rows_total = 0;
   DevState* host_st = nullptr;  // pinned
   // per-launch event timing (la_step_profile)
   struct ProfRec {
@@ -450,6 +455,7 @@ int enqueue_step(la_session* ss) {
   io.amax = ss->at<int32_t>(ss->v.amax);
   io.max_new = ss->p.max_new;
   io.eos = ss->p.eos_id;
+  io.gmax = s.G;
   io.logits = ss->at<float>(ss->v.logits);
   io.V = s.V;
   io.temp = ss->p.temperature;
@@ -457,7 +463,8 @@ int enqueue_step(la_session* ss) {
   io.top_k = ss->p.top_k < s.V ? ss->p.top_k : 0;
   io.top_p = ss->p.top_p > 0.f && ss->p.top_p < 1.f ? ss->p.top_p : 1.f;
 
-  const double R = s.M, ES = (double)dtype_size(dt);
+  const int Mc = ss->lay.M;  // rows of this step (the layout's G may be below s.G)
+  const double R = Mc, ES = (double)dtype_size(dt);
   LA_KP(LA_PROF_BOOK, 0, 0, launch_gather(pool, io, ss->lay, st), "gather");
   const size_t es = dtype_size(dt);
   const size_t cache_bytes = (size_t)s.L * s.Hkv * s.ld_ctx * s.hd * es;
@@ -472,7 +479,7 @@ int enqueue_step(la_session* ss) {
   LA_K(trace_copy(ss, io.pos, (size_t)s.M * 4), "trace");
   LA_K(trace_copy(ss, ss->at(ss->v.kc), cache_bytes), "trace");
   LA_K(trace_copy(ss, ss->at(ss->v.vc), cache_bytes), "trace");
-  int rc = enqueue_forward(ss, s.M, false);
+  int rc = enqueue_forward(ss, Mc, false);
   if (rc != LA_OK) return rc;
   LA_K(trace_copy(ss, ss->at(ss->v.kb), blk_bytes), "trace");
   LA_K(trace_copy(ss, ss->at(ss->v.vb), blk_bytes), "trace");
@@ -480,14 +487,14 @@ int enqueue_step(la_session* ss) {
   float* x = ss->at<float>(ss->v.x);
   void* h = ss->at(ss->v.h);
   GemmDesc g{};
-  g.x = h; g.rows = s.M; g.rows_pad = s.M; g.K = s.d; g.nseg = 1;
+  g.x = h; g.rows = Mc; g.rows_pad = Mc; g.K = s.d; g.nseg = 1;
   g.seg[0] = {m->lm_head, s.V}; g.N = s.V; g.sp = s.sp_lm;
   g.part = ss->at<float>(ss->v.logits);
   LA_KP(LA_PROF_LMHEAD, ((double)s.V * s.d + R * s.d) * ES + R * s.V * 4.0,
         2.0 * R * s.V * s.d, launch_gemm(g, dt, st), "gemm_lm_head");
   LA_K(trace_copy(ss, ss->at(ss->v.logits), (size_t)s.M * s.V * 4), "trace");
   LA_KP(LA_PROF_ARGMAX, R * s.V * 4.0, 0,
-        launch_argmax(ss->at<float>(ss->v.logits), s.M, s.V, ss->at<int32_t>(ss->v.amax), st),
+        launch_argmax(ss->at<float>(ss->v.logits), Mc, s.V, ss->at<int32_t>(ss->v.amax), st),
         "argmax");
   if (io.temp > 0.f)
     LA_KP(LA_PROF_BOOK, 0, 0, launch_sample_verify(io, ss->lay, st), "sample_verify");
@@ -575,14 +582,51 @@ int la_session_rows(const la_session* s, int32_t* rows) {
 
 static void session_destroy(la_session* s) {
   if (!s) return;
-  if (s->exec) hipGraphExecDestroy(s->exec);
-  if (s->graph) hipGraphDestroy(s->graph);
+  for (hipGraphExec_t e : s->execs)
+    if (e) hipGraphExecDestroy(e);
+  for (hipGraph_t g : s->graphs)
+    if (g) hipGraphDestroy(g);
   if (s->host_st) hipHostFree(s->host_st);
   for (hipEvent_t e : s->evs) hipEventDestroy(e);
   delete s;
 }
 
 void la_session_free(la_session* s) { session_destroy(s); }
+
+// Capture the step at the session's current layout into a graph (once per
+// verification width).
+static int capture_step(la_session* ss) {
+  const int g = ss->lay.G;
+  if (ss->execs[g]) return LA_OK;
+  hipStream_t st = ss->stream;
+  hipError_t e = hipStreamBeginCapture(st, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) return fail(LA_EHIP, std::string("hipStreamBeginCapture: ") + hipGetErrorString(e));
+  const int rc = enqueue_step(ss);
+  hipGraph_t gr = nullptr;
+  e = hipStreamEndCapture(st, &gr);
+  if (rc != LA_OK) {
+    if (gr) hipGraphDestroy(gr);
+    return rc;
+  }
+  if (e != hipSuccess) return fail(LA_EHIP, std::string("hipStreamEndCapture: ") + hipGetErrorString(e));
+  ss->graphs[g] = gr;
+  e = hipGraphInstantiate(&ss->execs[g], gr, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    ss->execs[g] = nullptr;
+    return fail(LA_EHIP, std::string("hipGraphInstantiate: ") + hipGetErrorString(e));
+  }
+  return LA_OK;
+}
+
+// Verification width of a step whose gather will take g candidates: the
+// most candidates (at most G) whose rows fit the same 16-row tiles.
+static int adaptive_width(const Shape& s, int g) {
+  const int n1 = s.N - 1;
+  const int tiles = (1 + (s.W + g) * n1 + 15) / 16;
+  int w = (16 * tiles - 1) / n1 - s.W;
+  if (w > s.G) w = s.G;
+  return w < g ? g : w;
+}
 
 int la_prefill(la_model* m, const la_decode_params* p, const int32_t* prompt, int32_t n_prompt,
                const int32_t* init_window, void* dev_workspace, size_t ws_bytes, void* hip_stream,
@@ -672,18 +716,19 @@ int la_prefill(la_model* m, const la_decode_params* p, const int32_t* prompt, in
   }
   LA_PF(hipStreamSynchronize(st));
 
+  ss->graphs.assign((size_t)s.G + 1, nullptr);
+  ss->execs.assign((size_t)s.G + 1, nullptr);
   if (graph) {
-    LA_PF(hipStreamBeginCapture(st, hipStreamCaptureModeThreadLocal));
-    rc = enqueue_step(ss);
-    hipGraph_t gr = nullptr;
-    hipError_t ec = hipStreamEndCapture(st, &gr);
-    if (rc != LA_OK) {
-      if (gr) hipGraphDestroy(gr);
-      return bail(rc);
+    // every width a step can take, captured now so that no step pays for a
+    // capture (with LA_ADAPTIVE_G one per 16-row tile count)
+    const bool adaptive = (p->flags & LA_ADAPTIVE_G) != 0;
+    for (int g = adaptive ? 0 : s.G; g <= s.G; ++g) {
+      const int w = adaptive ? adaptive_width(s, g) : s.G;
+      ss->lay = RowLayout{s.N, s.W, w, 1 + (s.W + w) * n1};
+      rc = capture_step(ss);
+      if (rc != LA_OK) return bail(rc);
     }
-    LA_PF(ec);
-    ss->graph = gr;
-    LA_PF(hipGraphInstantiate(&ss->exec, ss->graph, nullptr, nullptr, 0));
+    ss->lay = RowLayout{s.N, s.W, s.G, s.M};
   }
   ss->P_host = n_prompt - 1;
   *out = ss;
@@ -713,6 +758,13 @@ static int step_impl(la_session* s, int32_t* out_tokens, int32_t out_cap, int32_
   if (s->P_host + max_offset(s->s) + 1 > s->p.max_ctx)
     return fail(LA_ECTX, "context full: step would pass max_ctx");
   int rc = LA_OK;
+  // the step's layout: the full width, or with LA_ADAPTIVE_G the width the
+  // candidates found for this step's token need (the previous step counted
+  // them; the first step takes the full width)
+  int gw = s->s.G;
+  if ((s->p.flags & LA_ADAPTIVE_G) && !prof && !trace && s->rows_total > 0)
+    gw = adaptive_width(s->s, s->host_st->next_g);
+  s->lay = RowLayout{s->s.N, s->s.W, gw, 1 + (s->s.W + gw) * (s->s.N - 1)};
   if (prof) {
     s->prof_on = true;
     s->recs.clear();
@@ -724,9 +776,12 @@ static int step_impl(la_session* s, int32_t* out_tokens, int32_t out_cap, int32_
     s->trace_off = 0;
     rc = enqueue_step(s);
     s->trace = nullptr;
-  } else if (s->exec) {
-    hipError_t e = hipGraphLaunch(s->exec, s->stream);
-    if (e != hipSuccess) rc = fail(LA_EHIP, std::string("hipGraphLaunch: ") + hipGetErrorString(e));
+  } else if (!(s->p.flags & LA_NO_GRAPH)) {
+    rc = capture_step(s);  // a width not seen yet (LA_ADAPTIVE_G) is captured now
+    if (rc == LA_OK) {
+      hipError_t e = hipGraphLaunch(s->execs[gw], s->stream);
+      if (e != hipSuccess) rc = fail(LA_EHIP, std::string("hipGraphLaunch: ") + hipGetErrorString(e));
+    }
   } else {
     rc = enqueue_step(s);
   }
@@ -756,6 +811,7 @@ static int step_impl(la_session* s, int32_t* out_tokens, int32_t out_cap, int32_
       prof->flops[r.kind] += r.flops;
     }
   }
+  s->rows_total += s->lay.M;
   const int n = s->host_st->n_out;
   for (int i = 0; i < n; ++i) out_tokens[i] = s->host_st->out[i];
   *n_out = n;
@@ -806,6 +862,7 @@ int la_pool_stats(const la_session* s, la_pool_stats_t* out) {
   out->evictions = h.stats[ST_EVICT];
   out->gathers_nonempty = h.stats[ST_GATHER_NE];
   out->cand_total = h.stats[ST_CAND_TOTAL];
+  out->rows_total = s->rows_total;
   return LA_OK;
 }
 

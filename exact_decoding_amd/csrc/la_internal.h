@@ -43,6 +43,7 @@ struct DevState {
   int32_t done;        // 1 once max_new or EOS is reached
   int32_t n_out;       // tokens emitted by the last step
   int32_t out[LA_MAX_N];
+  int32_t next_g;      // candidates the next step will gather (min(bucket of cur, G))
   int32_t ncand;       // candidates gathered this step
   int32_t commit_p;    // P before the last step's commit
   int32_t commit_n;    // rows committed by the last step
@@ -203,6 +204,7 @@ struct StepIO {
   int32_t* pos;   // [M]
   const int32_t* amax;  // [M]
   int max_new, eos;
+  int gmax;       // the session's G (the layout's G may be smaller, LA_ADAPTIVE_G)
   // sampling verification ([LD] §3.4 "Sampling verification (Algorithm 4)");
   // temp == 0: greedy verification
   const float* logits;  // [M][V]

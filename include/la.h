@@ -90,6 +90,17 @@ typedef struct {
  *              pages contrast first-token matching with longer prefixes
  *              ([LD] Table 3, "What is not ablated").  Output tokens are
  *              unchanged; it matters only when pool_cap > G.
+ *            LA_ADAPTIVE_G: a step's verification branch holds only the
+ *              candidate rows its GEMM row tiles need: the step after one
+ *              that found g candidates for its next token processes
+ *              1 + (W + G')(N-1) rows, G' the most candidates (at most G)
+ *              that fit the same 16-row tiles as g (the pages verify "up to
+ *              G" candidates, [LD] §3.4 "N-gram selection from the pool").
+ *              Candidate rows past the pool's candidates are padding that
+ *              can never be accepted, so tokens, steps and every pool
+ *              counter equal those of the fixed-G step; only the rows
+ *              computed change (rows_total in la_pool_stats_t).  Graph mode
+ *              captures one step per row-tile count as it is first needed.
  * temperature  0: greedy verification ([LD] §3.4 "Greedy verification
  *              algorithm (Algorithm 3)").  > 0: sampling verification
  *              ([LD] §3.4 "Sampling verification (Algorithm 4)") against
@@ -123,6 +134,7 @@ typedef struct {
 #define LA_NO_GRAPH 8u
 #define LA_POOL_LRU 16u
 #define LA_POOL_CONTEXT 32u
+#define LA_ADAPTIVE_G 64u
 
 /* Statistics since prefill ([LD] §3.4 "Scaling Law": S = tokens / steps). */
 typedef struct {
@@ -131,6 +143,7 @@ typedef struct {
   int64_t pool_ngrams, pool_keys_nonempty;
   int64_t inserts, dup_skips, evictions;
   int64_t gathers_nonempty, cand_total;
+  int64_t rows_total; /* block rows the steps' forward passes processed */
 } la_pool_stats_t;
 
 typedef struct la_model la_model;
@@ -250,7 +263,8 @@ int la_step_trace(la_session* s, int32_t* out_tokens, int32_t out_cap, int32_t* 
                   void* dev_trace, size_t bytes);
 int la_step_trace_bytes(const la_session* s, size_t* bytes);
 
-/* Rows in one step (M) of this session. */
+/* Rows in one step (M = 1 + (W+G)(N-1)) of this session; with LA_ADAPTIVE_G
+ * the most rows a step processes. */
 int la_session_rows(const la_session* s, int32_t* rows);
 
 void la_session_free(la_session* s);

@@ -341,6 +341,7 @@ class DecodeResult:
     step_rows: list[np.ndarray]         # per step: block-row tokens
     pool: NGramPool | None = None
     margins: list[float] = dataclasses.field(default_factory=list)  # sampling: per step
+    ncand: list[int] = dataclasses.field(default_factory=list)      # candidates per step
 
     @property
     def S(self) -> float:
@@ -493,6 +494,7 @@ def lookahead(model: OracleModel, prompt, N: int, W: int, G: int, max_new: int,
         res.steps += 1
         res.accepted.append(acc)
         res.emitted.append(len(step_emit))
+        res.ncand.append(len(cands))
         prev = int(emit[-2]) if len(emit) >= 2 else int(cur)
         cur = bonus
         if eos_id >= 0 and out and out[-1] == eos_id:

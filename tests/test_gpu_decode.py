@@ -211,6 +211,52 @@ def test_tiny_wide_window_pool_matches_oracle(tiny, N, W, G):
     assert st["inserts"] + st["dup_skips"] == n_prompt_ngrams + W * st["steps"]
 
 
+def _adaptive_rows(ncand, N, W, G):
+    """Rows an LA_ADAPTIVE_G session processes: the first step the full
+    width; every later step the most candidate rows (at most G) that fit the
+    16-row tiles the step's candidate count needs."""
+    n1 = N - 1
+    full = 1 + (W + G) * n1
+    rows = full
+    for g in ncand[1:]:
+        tiles = -(-(1 + (W + g) * n1) // 16)
+        w = min(G, (16 * tiles - 1) // n1 - W)
+        rows += 1 + (W + max(w, g)) * n1
+    return rows
+
+
+@pytest.mark.parametrize("graph", [True, False])
+@pytest.mark.parametrize("N,W,G,prompt_ref", [(3, 4, 4, True), (4, 3, 6, True), (5, 2, 7, False),
+                                              (3, 70, 4, True), (4, 2, 20, True)])
+def test_tiny_adaptive_g_matches_oracle(tiny, N, W, G, prompt_ref, graph):
+    """LA_ADAPTIVE_G: candidate rows past the pool's candidates are left out,
+    which changes nothing a step computes for the rows that remain, so every
+    token, the tokens of each step, the accepted-length histogram and every
+    pool counter equal the oracle's fixed-G run; the rows processed follow
+    the oracle's candidate count of each step."""
+    s, w, gm, om = tiny
+    n_new = 32
+    prompt = synth.prompt_motif(s.vocab, seed=1)
+    win = synth.gen_window(N, W, s.vocab, seed=2)
+    print(f"tiny fp32 adaptive G N={N} W={W} G={G} ref={prompt_ref} graph={graph}", flush=True)
+    ref = la.lookahead(om, prompt, N, W, G, n_new, win, prompt_ref=prompt_ref)
+    ses = gm.session(prompt, N, W, G, n_new, window=win, prompt_ref=prompt_ref, graph=graph,
+                     adaptive_g=True)
+    ses.decode()
+    st = ses.stats()
+    ses.close()
+    assert ses.tokens == ref.tokens
+    assert ses.per_step == ref.emitted
+    assert st["steps"] == ref.steps
+    assert [st["accept_hist"][j] for j in range(N)] == [ref.accepted.count(j) for j in range(N)]
+    assert st["inserts"] == ref.pool.inserts and st["dup_skips"] == ref.pool.dup_skips
+    assert st["evictions"] == ref.pool.evictions
+    assert st["pool_ngrams"] == ref.pool.n_ngrams() and st["pool_keys_nonempty"] == ref.pool.n_keys()
+    assert st["cand_total"] == sum(ref.ncand)
+    assert st["rows_total"] == _adaptive_rows(ref.ncand, N, W, G)
+    assert st["rows_total"] <= st["steps"] * (1 + (W + G) * (N - 1))
+
+
 def test_context_full_is_reported(tiny):
     """A step that would write past max_ctx is refused with LA_ECTX before any
     device work; the tokens emitted until then are the AR stream's prefix."""
@@ -378,3 +424,29 @@ def test_bf16_pool_variants_bit_exact(graph):
         assert ses.decode() == ar_toks
         ses.close()
     gm.close()
+
+
+@pytest.mark.parametrize("name,N,W,G", [("small_bf16", 5, 7, 7), ("small_gqa_bf16", 4, 5, 9)])
+def test_bf16_adaptive_g_bit_exact(name, N, W, G):
+    """bf16 models: the LA_ADAPTIVE_G stream is the same engine's AR stream
+    bit for bit, and the same as the fixed-G lookahead stream, with no more
+    rows processed."""
+    s = synth.SHAPES[name]
+    gm = Model(s, synth.gen_weights(s, 0))
+    prompt = synth.prompt_zipf_spans(s.vocab, length=64, seed=1)
+    win = synth.gen_window(N, W, s.vocab, seed=2)
+    n_new = 48
+    out = {}
+    for adaptive in (False, True):
+        ses = gm.session(prompt, N, W, G, n_new, window=win, prompt_ref=True, adaptive_g=adaptive)
+        out[adaptive] = (ses.decode(), ses.stats())
+        ses.close()
+    ar = gm.session(prompt, N, W, G, n_new, ar=True)
+    ar_toks = ar.decode()
+    ar.close()
+    gm.close()
+    assert out[True][0] == ar_toks == out[False][0]
+    fixed, adapt = out[False][1], out[True][1]
+    for k in ("steps", "tokens", "inserts", "dup_skips", "evictions", "cand_total"):
+        assert fixed[k] == adapt[k], k
+    assert adapt["rows_total"] <= fixed["rows_total"] == fixed["steps"] * (1 + (W + G) * (N - 1))

@@ -180,16 +180,17 @@ def _layer_check(s, w, gm, prompt, N, W, G, layers, warm_steps=3):
     assert err <= 1e-4
 
 
-def _bit_exact(gm, prompt, N, W, G, n_new, vocab):
+def _bit_exact(gm, prompt, N, W, G, n_new, vocab, adaptive=False):
     win = synth.gen_window(N, W, vocab, seed=2)
-    ses = gm.session(prompt, N, W, G, n_new, window=win, prompt_ref=True)
+    ses = gm.session(prompt, N, W, G, n_new, window=win, prompt_ref=True, adaptive_g=adaptive)
     la_toks = ses.decode()
     st = ses.stats()
     ses.close()
     ar = gm.session(prompt, N, W, G, n_new, ar=True)
     ar_toks = ar.decode()
     ar.close()
-    _log(f"lookahead: {st['tokens']} tokens in {st['steps']} steps (S = {st['tokens'] / st['steps']:.3f})")
+    _log(f"lookahead{' (adaptive G)' if adaptive else ''}: {st['tokens']} tokens in {st['steps']} "
+         f"steps (S = {st['tokens'] / st['steps']:.3f}), {st['rows_total']} rows")
     assert la_toks == ar_toks
     assert 1 <= st["tokens"] / st["steps"] <= N
 
@@ -209,6 +210,7 @@ def test_llama7b_full():
     s, w, gm = _build("llama7b")
     prompt = synth.prompt_zipf_spans(s.vocab, length=128, seed=1)
     _bit_exact(gm, prompt, 5, 15, 15, 256, s.vocab)
+    _bit_exact(gm, prompt, 5, 15, 15, 256, s.vocab, adaptive=True)
     _layer_check(s, w, gm, prompt, 5, 15, 15, range(s.n_layers))
     _oracle_check(s, w, gm, prompt, 64, 5, min_decided=8)
     gm.close()

@@ -32,7 +32,8 @@ def test_flag_values_match_header():
     defs = dict(re.findall(r"#define (LA_[A-Z_]+) (\d+)u", src))
     assert defs == {"LA_PROMPT_REF": str(B.LA_PROMPT_REF), "LA_AR": str(B.LA_AR),
                     "LA_NO_GRAPH": str(B.LA_NO_GRAPH), "LA_POOL_LRU": str(B.LA_POOL_LRU),
-                    "LA_POOL_CONTEXT": str(B.LA_POOL_CONTEXT)}
+                    "LA_POOL_CONTEXT": str(B.LA_POOL_CONTEXT),
+                    "LA_ADAPTIVE_G": str(B.LA_ADAPTIVE_G)}
 
 
 def _model(dtype=B.LA_BF16, L=2, d=512, H=4, Hkv=4, hd=128, F=1408, V=4000):
@@ -81,8 +82,8 @@ def test_session_bytes_and_param_validation():
         assert B.la_session_bytes(m, p_k) == n
     for bad in [B.DecodeParams(1, 4, 4, 0, 100, 10, -1, 0), B.DecodeParams(17, 4, 4, 0, 100, 10, -1, 0),
                 B.DecodeParams(3, -1, 4, 0, 100, 10, -1, 0), B.DecodeParams(3, 4, 4, 0, 100, 0, -1, 0),
-                B.DecodeParams(3, 4, 4, 0, 100, 10, 4000, 0), B.DecodeParams(3, 4, 4, 0, 100, 10, -1, 64),
-                B.DecodeParams(3, 4, 4, 0, 100, 10, -1, 64 * 2),
+                B.DecodeParams(3, 4, 4, 0, 100, 10, 4000, 0), B.DecodeParams(3, 4, 4, 0, 100, 10, -1, 128),
+                B.DecodeParams(3, 4, 4, 0, 100, 10, -1, 128 * 2),
                 B.DecodeParams(2, 0, 1025, 0, 4000, 10, -1, 0),
                 B.DecodeParams(16, 100, 100, 0, 100, 10, -1, 0),
                 # sampling: negative or non-finite temperature, reserved field set

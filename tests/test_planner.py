@@ -61,3 +61,31 @@ def test_rejects_bad_arguments():
         planner.expected_tokens(1.5, 4, 2)
     with pytest.raises(ValueError):
         planner.compression(0.4, 5, 2, 0.5)
+
+
+def test_fit_reproduces_oracle_compressions():
+    """Eq. 5/7 fitted to the step compressions of the oracle's lookahead runs
+    on the two small random-init models that repeat n-grams
+    (tests/golden/scaling_points.json, written by make_scaling_points.py
+    from oracle/ alone: N in {3, 4, 5}, W = G in {1 .. 15}, 16 prompts of 128
+    tokens).  One (alpha, f) per model reproduces its 24 measured S values
+    (1.7 to 3.7) with a root-mean-square error below 0.2 and none off by
+    more than 0.4; S grows with W at every N, as the model's diminishing
+    returns in b say it should."""
+    import json
+    import math
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "scaling_points.json")
+    data = json.load(open(path))
+    for name, pts in data["models"].items():
+        trip = [(p["N"], p["W"], p["S"]) for p in pts]
+        assert all(p["S"] == p["tokens"] / p["steps"] for p in pts)
+        alpha, f = planner.fit(trip)
+        assert 0.0 < alpha < 1.0 and f >= 1.0
+        res = [planner.compression(alpha, n, w, f) - s for n, w, s in trip]
+        rms = math.sqrt(sum(r * r for r in res) / len(res))
+        assert rms < 0.2, (name, alpha, f, rms)
+        assert max(abs(r) for r in res) < 0.4, (name, alpha, f, res)
+        for N in (3, 4, 5):
+            s_n = [s for n, w, s in trip if n == N]
+            assert s_n[-1] > s_n[0]
