@@ -154,17 +154,65 @@ def timed_steps(sessions_factory, K, sync):
     return dt, tokens
 
 
+def host_cpu():
+    """The host's CPU model (from /proc/cpuinfo) and the cores this process
+    may run on (its affinity mask)."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:  # pragma: no cover
+        pass
+    return model, len(os.sched_getaffinity(0))
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def cpu_tiny():
+    """The oracle (as it stands) on the tiny fp32 workload: whole greedy AR
+    (32 new tokens) and whole lookahead (N=3, W=4, G=4, prompt as reference)
+    after the 16-token motif prompt, on one BLAS thread and on all of them."""
+    import synth
+    from oracle import lookahead as la
+    from oracle.model import OracleModel
+    from threadpoolctl import threadpool_limits
+    s = synth.SHAPES["tiny"]
+    om = OracleModel(s, synth.gen_weights(s, 0))
+    prompt = synth.prompt_motif(s.vocab, seed=1)
+    win = synth.gen_window(3, 4, s.vocab, seed=2)
+    out = {}
+    for label, nthreads in (("1_thread", 1), ("all_threads", host_cpu()[1])):
+        with threadpool_limits(limits=nthreads):
+            t0 = time.perf_counter()
+            ar = la.greedy_ar(om, prompt, 32)
+            t_ar = time.perf_counter() - t0
+            t0 = time.perf_counter()
+            r = la.lookahead(om, prompt, 3, 4, 4, 32, win, prompt_ref=True)
+            t_la = time.perf_counter() - t0
+        out[label] = {"threads": nthreads, "ar_tokens_per_s": len(ar.tokens) / t_ar,
+                      "lookahead_tokens_per_s": len(r.tokens) / t_la, "lookahead_S": r.S,
+                      "lookahead_equals_ar": r.tokens == ar.tokens,
+                      "pool": {"inserts": r.pool.inserts, "dup_skips": r.pool.dup_skips,
+                               "evictions": r.pool.evictions, "ngrams": r.pool.n_ngrams()}}
+    return out
+
+
 def cpu_baseline(shape, weights, prompt, n_tokens):
     """Oracle greedy AR (as it stands) on a bounded sample: the first
     `n_tokens` decode steps after the prompt, prefill excluded from timing."""
     import numpy as np
     from oracle.model import OracleModel, causal_vis, argmax_lowest
     from oracle import lookahead as la
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
+    cpu_model, host_cores = host_cpu()
+    cores = min(blas_threads(), host_cores)
     om = OracleModel(shape, weights)
     # keep decoded float64 weights only when the host has room for them
     try:
@@ -185,7 +233,9 @@ def cpu_baseline(shape, weights, prompt, n_tokens):
     return {"value": n_tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{shape.name} greedy AR, {n_tokens} decode tokens after the "
                       f"{len(prompt)}-token prompt (prefill untimed), float64 numpy, "
-                      f"weights {'decoded once' if om.keep else 'decoded per call'}"}
+                      f"weights {'decoded once' if om.keep else 'decoded per call'}",
+            "cpu_model": cpu_model, "host_cores": host_cores,
+            "tiny_fp32": cpu_tiny()}
 
 
 SWEEP_N = (3, 5, 7)
