@@ -21,7 +21,7 @@ LA_MAX_N = 16
 LA_PROBE_BLOCKS = 2048
 LA_NOALLOC_SCRATCH_BYTES = 32 << 20
 LA_PROMPT_REF, LA_AR, LA_NO_GRAPH, LA_POOL_LRU, LA_POOL_CONTEXT = 1, 2, 8, 16, 32
-LA_ADAPTIVE_G = 64
+LA_ADAPTIVE_G, LA_DEBUG_LOGITS = 64, 4
 
 EXPORTS = [
     "la_model_load", "la_model_free", "la_session_bytes", "la_prefill", "la_step",

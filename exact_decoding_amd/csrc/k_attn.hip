@@ -738,7 +738,31 @@ __global__ __launch_bounds__(1024) void k_argmax(const float* logits, int V, int
   }
 }
 
+// Row argmax from the LM head's per-block keys: one wave per row, the
+// largest key (any order gives it), its column.
+__global__ __launch_bounds__(64) void k_argmax_keys(const unsigned long long* keys, int nblk,
+                                                    int32_t* out) {
+  const int m = blockIdx.x, lane = threadIdx.x;
+  const unsigned long long* row = keys + (size_t)m * nblk;
+  unsigned long long best = 0;
+  for (int b = lane; b < nblk; b += 64) best = row[b] > best ? row[b] : best;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const unsigned int lo = __shfl_xor((unsigned int)best, o, 64);
+    const unsigned int hi = __shfl_xor((unsigned int)(best >> 32), o, 64);
+    const unsigned long long k = ((unsigned long long)hi << 32) | lo;
+    best = k > best ? k : best;
+  }
+  if (lane == 0) out[m] = (int32_t)(0xFFFFFFFFu - (unsigned int)best);
+}
+
 }  // namespace
+
+hipError_t launch_argmax_keys(const unsigned long long* keys, int rows, int nblk, int32_t* out,
+                              hipStream_t st) {
+  hipLaunchKernelGGL(k_argmax_keys, dim3(rows), dim3(64), 0, st, keys, nblk, out);
+  return hipGetLastError();
+}
 
 int attn_uses_mfma(int dtype, int hd) { return dtype == LA_BF16 && hd == 128; }
 

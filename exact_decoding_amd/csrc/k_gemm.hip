@@ -66,6 +66,38 @@ constexpr int XR = 3;  // LDS stages of the x tile
 
 __device__ __forceinline__ int xswz(int row, int piece) { return piece ^ ((row >> 1) & 7); }
 
+// The argmax keys of column block b (one whole block) for rows row0 ..
+// row0 + nr - 1, from its values in LDS: row rr, local column c at
+// vs[(c / 32) * ld_wave + rr * ld_row + c % 32].  Each row's 128 columns are
+// cut into 16 runs of 8 taken by different threads (partial keys in kp,
+// LDS, nr * 16 of them), then thread rr takes the largest of its row's 16.
+// The caller has synchronised the workgroup after writing vs.
+__device__ __forceinline__ void block_row_keys(const GemmDesc& g, const float* vs, int ld_wave,
+                                               int ld_row, unsigned long long* kp, int b,
+                                               int row0, int nr) {
+  const int col0 = b * NWG;
+  for (int t = threadIdx.x; t < nr * 16; t += blockDim.x) {
+    const int rr = t >> 4, c0 = (t & 15) * 8;
+    unsigned long long best = 0;
+#pragma unroll
+    for (int c = c0; c < c0 + 8; ++c) {
+      if (col0 + c < g.N) {
+        const unsigned long long k =
+            argmax_key(vs[(c >> 5) * ld_wave + rr * ld_row + (c & 31)], col0 + c);
+        best = k > best ? k : best;
+      }
+    }
+    kp[t] = best;
+  }
+  __syncthreads();
+  for (int rr = threadIdx.x; rr < nr; rr += blockDim.x) {
+    unsigned long long best = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) best = kp[rr * 16 + j] > best ? kp[rr * 16 + j] : best;
+    g.amax_keys[(size_t)(row0 + rr) * g.sp.nblk + b] = best;
+  }
+}
+
 template <int MT>
 __global__ __launch_bounds__(320) void k_gemm_bf16(GemmDesc g) {
   constexpr int XSTAGE = MT * 16 * 64;  // bf16 per x stage
@@ -257,6 +289,7 @@ __global__ __launch_bounds__(320) void k_gemm_bf16(GemmDesc g) {
   // with this run, so its piece is slot 0.
   auto store_block = [&](const f32x4_t (&a)[MT][2], int slot, int sbase, int segn, int nl)
       __attribute__((always_inline)) {
+    if (!g.part) return;
     float* out = g.part + (size_t)slot * g.rows_pad * g.N;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
@@ -284,7 +317,22 @@ __global__ __launch_bounds__(320) void k_gemm_bf16(GemmDesc g) {
   } else {
     store_block(acc, slotA, sbA, segnA, nlA);
   }
+  if (g.amax_keys) {
+    // whole-block plan: this block's values to LDS as [16 * MT rows][128 columns]
+    float* vs = (float*)park;
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vs[(i * 16 + q * 4 + e) * NWG + wave * 32 + tt * 16 + r] = acc[i][tt][e];
+  }
   }  // consumers
+  if (g.amax_keys) {
+    __syncthreads();  // every wave's values in park; the x stages are free
+    block_row_keys(g, (const float*)park, 32, NWG, (unsigned long long*)xs, bA, row0,
+                   min(MT * 16, g.rows - row0));
+  }
 }
 
 // Four symmetric waves, one per SIMD (so each may hold up to 512 registers).
@@ -490,6 +538,7 @@ void k_gemm4(GemmDesc g) {
   // of rows l/8, l/8 + 8, ...
   const bool vec_ok = (g.N & 3) == 0;
   auto store_rows = [&](int slot, int sbase, int segn, int nl) __attribute__((always_inline)) {
+    if (!g.part) return;
     float* out = g.part + (size_t)slot * g.rows_pad * g.N;
     const int c4 = (lane & 7) * 4;
     const int nloc = nl + c4;
@@ -526,6 +575,13 @@ void k_gemm4(GemmDesc g) {
     park_acc();
     wave_lds_sync();
     store_rows(slotA, sbA, segnA, nlA);
+  }
+  if (g.amax_keys) {
+    // whole-block plan: the four waves' parked columns (wave w's region holds
+    // columns 32w .. 32w + 31 at row stride PKS); the x stages are free
+    __syncthreads();
+    block_row_keys(g, park, MT * 16 * PKS, PKS, (unsigned long long*)xs, bA, row0,
+                   min(MT * 16, g.rows - row0));
   }
 }
 
@@ -610,6 +666,9 @@ hipError_t launch_gemm(const GemmDesc& g, int dtype, hipStream_t st) {
     return hipGetLastError();
   }
   if (g.sp.nblk != (g.N + NWG - 1) / NWG || g.sp.nch != g.K / KC) return hipErrorInvalidValue;
+  // row maxima need whole column blocks (one piece each, one block a workgroup)
+  if (g.amax_keys && (g.sp.np != 1 || g.sp.G != g.sp.nblk || g.nseg != 1)) return hipErrorInvalidValue;
+  if (!g.part && !g.amax_keys) return hipErrorInvalidValue;
   const int mblk = (g.rows + 127) / 128;
   const int rows_last = g.rows - (mblk - 1) * 128;
   // the row-tile count only changes how many rows one workgroup carries, not

@@ -104,7 +104,7 @@ struct WsPlan {
 };
 
 struct Views {
-  size_t x, h, q, att, att_part, act, part, logits, amax, kc, vc, kb, vb, rope, pool_tok, pool_cnt,
+  size_t x, h, q, att, att_part, act, part, logits, amax, amax_keys, kc, vc, kb, vb, rope, pool_tok, pool_cnt,
       pool_head, pool_ctx, win, cand, ids, pos, prompt, st, total;
 };
 
@@ -177,6 +177,7 @@ Views plan_views(const Shape& s) {
   v.part = w.take(part);
   v.logits = w.take((size_t)s.M * s.V * 4);
   v.amax = w.take((size_t)s.M * 4);
+  v.amax_keys = w.take((size_t)s.M * s.sp_lm.nblk * 8);
   const size_t kvb = (size_t)s.L * s.Hkv * s.ld_ctx * s.hd * es;
   v.kc = w.take(kvb);
   v.vc = w.take(kvb);
@@ -210,7 +211,7 @@ int check_params(const la_model* m, const la_decode_params* p) {
   if (p->max_new < 1) return fail(LA_EINVAL, "max_new must be >= 1");
   if (p->eos_id >= m->d.vocab) return fail(LA_EINVAL, "eos_id out of range");
   if (p->flags & ~(LA_PROMPT_REF | LA_AR | LA_NO_GRAPH | LA_POOL_LRU | LA_POOL_CONTEXT |
-                   LA_ADAPTIVE_G))
+                   LA_ADAPTIVE_G | LA_DEBUG_LOGITS))
     return fail(LA_EINVAL, "unknown flags");
   const long long W = ar ? 0 : p->W, G = ar ? 0 : p->G;
   const long long M = 1 + (W + G) * (p->N - 1);
@@ -273,6 +274,11 @@ struct la_session {
 };
 
 namespace {
+
+// Whether every step leaves the logits in the workspace (la_debug_logits).
+bool session_keeps_logits(const la_session* ss) {
+  return ss->s.dt != LA_BF16 || (ss->p.flags & LA_DEBUG_LOGITS) || ss->p.temperature > 0.f;
+}
 
 hipError_t launch_checked(hipError_t e, const char* what, hipStream_t st) {
   if (e != hipSuccess) return e;
@@ -489,13 +495,25 @@ int enqueue_step(la_session* ss) {
   GemmDesc g{};
   g.x = h; g.rows = Mc; g.rows_pad = Mc; g.K = s.d; g.nseg = 1;
   g.seg[0] = {m->lm_head, s.V}; g.N = s.V; g.sp = s.sp_lm;
-  g.part = ss->at<float>(ss->v.logits);
-  LA_KP(LA_PROF_LMHEAD, ((double)s.V * s.d + R * s.d) * ES + R * s.V * 4.0,
+  // bf16: the LM head leaves each row's argmax as one key per 128-column
+  // block, and writes the logits only when they are wanted (sampling
+  // verification reads them; LA_DEBUG_LOGITS and the trace keep them)
+  const bool keys = dt == LA_BF16;
+  const bool logits = !keys || session_keeps_logits(ss) || ss->trace;
+  g.part = logits ? ss->at<float>(ss->v.logits) : nullptr;
+  g.amax_keys = keys ? ss->at<unsigned long long>(ss->v.amax_keys) : nullptr;
+  LA_KP(LA_PROF_LMHEAD, ((double)s.V * s.d + R * s.d) * ES + (logits ? R * s.V * 4.0 : 0.0),
         2.0 * R * s.V * s.d, launch_gemm(g, dt, st), "gemm_lm_head");
   LA_K(trace_copy(ss, ss->at(ss->v.logits), (size_t)s.M * s.V * 4), "trace");
-  LA_KP(LA_PROF_ARGMAX, R * s.V * 4.0, 0,
-        launch_argmax(ss->at<float>(ss->v.logits), Mc, s.V, ss->at<int32_t>(ss->v.amax), st),
-        "argmax");
+  if (keys)
+    LA_KP(LA_PROF_ARGMAX, R * s.sp_lm.nblk * 8.0, 0,
+          launch_argmax_keys(ss->at<unsigned long long>(ss->v.amax_keys), Mc, s.sp_lm.nblk,
+                             ss->at<int32_t>(ss->v.amax), st),
+          "argmax");
+  else
+    LA_KP(LA_PROF_ARGMAX, R * s.V * 4.0, 0,
+          launch_argmax(ss->at<float>(ss->v.logits), Mc, s.V, ss->at<int32_t>(ss->v.amax), st),
+          "argmax");
   if (io.temp > 0.f)
     LA_KP(LA_PROF_BOOK, 0, 0, launch_sample_verify(io, ss->lay, st), "sample_verify");
   LA_KP(LA_PROF_BOOK, 0, 0, launch_verify(pool, io, ss->lay, st), "verify");
@@ -869,6 +887,8 @@ int la_pool_stats(const la_session* s, la_pool_stats_t* out) {
 int la_debug_logits(const la_session* s, float* out, int32_t rows) {
   if (!s || !out) return fail(LA_EINVAL, "null argument");
   if (rows < 1 || rows > s->s.M) return fail(LA_EINVAL, "rows must be in [1, M]");
+  if (!session_keeps_logits(s))
+    return fail(LA_ESTATE, "the session keeps no logits: prefill it with LA_DEBUG_LOGITS");
   LA_HIP(hipStreamSynchronize(s->stream));
   LA_HIP(hipMemcpy(out, s->at(s->v.logits), (size_t)rows * s->s.V * 4, hipMemcpyDeviceToHost));
   return LA_OK;

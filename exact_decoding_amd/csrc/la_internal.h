@@ -103,8 +103,25 @@ struct GemmDesc {
   int N;          // total columns (sum of segment rows)
   SplitPlan sp;   // how the (column block, K chunk) units are dealt out
   float* part;    // [sp.np][rows_pad][N]; the output itself when sp.np == 1
+                  // (null: no output, with amax_keys)
   int rows_pad;   // leading row count of part
+  // whole-block plans (sp.np == 1, bf16): each column block's row maxima as
+  // argmax keys, [rows][sp.nblk] (argmax_key); null: none
+  unsigned long long* amax_keys;
 };
+
+// Order-preserving 64-bit argmax key of logit v at column col: the larger
+// key has the larger value, and of equal values the lower column (the
+// argmax's ties go to the lowest id); -0 counts as +0.
+__host__ __device__ inline unsigned long long argmax_key(float v, int col) {
+  unsigned int u;
+  __builtin_memcpy(&u, &v, 4);
+  if ((u << 1) == 0u) u = 0u;
+  const unsigned int ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((unsigned long long)ord << 32) | (0xFFFFFFFFu - (unsigned int)col);
+}
+hipError_t launch_argmax_keys(const unsigned long long* keys, int rows, int nblk, int32_t* out,
+                              hipStream_t st);
 
 SplitPlan gemm_plan(int N, int K, int dtype);
 SplitPlan gemm_plan_whole(int N, int K);  // one workgroup per column block

@@ -68,18 +68,22 @@ class Model:
                 max_ctx: int | None = None, pool_cap: int = 0, eos_id: int = -1,
                 temperature: float = 0.0, seed: int = 0, top_k: int = 0,
                 top_p: float = 0.0, pool_lru: bool = False,
-                pool_context: bool = False, adaptive_g: bool = False) -> "Session":
+                pool_context: bool = False, adaptive_g: bool = False,
+                debug_logits: bool = False) -> "Session":
         """temperature 0: greedy; > 0: sampling verification with draws keyed
         by `seed`, optionally cut to the top_k tokens and then to a top_p share
         (0 = no cut; see la.h).  pool_lru: evict pool entries by recency
         instead of FIFO (LA_POOL_LRU); pool_context: select candidates by
         their context token first (LA_POOL_CONTEXT); adaptive_g: candidate
-        rows only as far as the step's candidates need (LA_ADAPTIVE_G)."""
+        rows only as far as the step's candidates need (LA_ADAPTIVE_G);
+        debug_logits: keep every step's logits for Session.logits
+        (LA_DEBUG_LOGITS)."""
         flags = (B.LA_PROMPT_REF if prompt_ref else 0) | (B.LA_AR if ar else 0)
         flags |= 0 if graph else B.LA_NO_GRAPH
         flags |= B.LA_POOL_LRU if pool_lru else 0
         flags |= B.LA_POOL_CONTEXT if pool_context else 0
         flags |= B.LA_ADAPTIVE_G if adaptive_g else 0
+        flags |= B.LA_DEBUG_LOGITS if debug_logits else 0
         if max_ctx is None:
             max_ctx = len(prompt) + max_new + N + W + 2
         p = B.DecodeParams(N, W, G, pool_cap, max_ctx, max_new, eos_id, flags,

@@ -71,6 +71,11 @@ typedef struct {
  *              kernels (W = G = 0 internally; one token per step).
  *            LA_NO_GRAPH: launch every step's kernels eagerly instead of
  *              replaying a captured HIP graph.
+ *            LA_DEBUG_LOGITS: every step leaves its rows' logits for
+ *              la_debug_logits.  Without it a bf16 session keeps them only
+ *              when it samples (temperature > 0): its LM head reduces each
+ *              row to its argmax and writes no logits (fp32 sessions keep
+ *              them always).
  *            LA_POOL_LRU: evict by recency instead of FIFO.  A suffix that
  *              is generated again (from the window or the prompt) becomes
  *              its bucket's newest entry, so a full bucket drops the one
@@ -131,6 +136,7 @@ typedef struct {
 
 #define LA_PROMPT_REF 1u
 #define LA_AR 2u
+#define LA_DEBUG_LOGITS 4u
 #define LA_NO_GRAPH 8u
 #define LA_POOL_LRU 16u
 #define LA_POOL_CONTEXT 32u
@@ -241,7 +247,8 @@ int la_step_profile(la_session* s, int32_t* out_tokens, int32_t out_cap, int32_t
 int la_pool_stats(const la_session* s, la_pool_stats_t* out);
 
 /* fp32 logits of the last step's M rows (rows <= M), row-major [rows][vocab],
- * copied to the host pointer `out`.  Test hook. */
+ * copied to the host pointer `out`.  Test hook.  LA_ESTATE for a bf16 session
+ * without LA_DEBUG_LOGITS that does not sample (it keeps no logits). */
 int la_debug_logits(const la_session* s, float* out, int32_t rows);
 
 /* One step, as la_step, run eagerly with a copy of every intermediate of

@@ -41,7 +41,8 @@ def test_tiny_fp32_matches_oracle(tiny, prompt_ref, graph):
     ar = la.greedy_ar(om, prompt, n_new)
     ref = la.lookahead(om, prompt, N, W, G, n_new, win, prompt_ref=prompt_ref, keep_logits=True)
     assert ref.tokens == ar.tokens
-    ses = gm.session(prompt, N, W, G, n_new, window=win, prompt_ref=prompt_ref, graph=graph)
+    ses = gm.session(prompt, N, W, G, n_new, window=win, prompt_ref=prompt_ref, graph=graph,
+                     debug_logits=True)
     first = ses.step()
     lg = ses.logits()
     np.testing.assert_allclose(lg, ref.step_logits[0], atol=1e-4, rtol=0)
@@ -92,11 +93,15 @@ def _bf16_case(name, N, W, G, n_new, prompt):
     la_toks = la_ses.decode()
     st = la_ses.stats()
     la_ses.close()
-    ar_ses = gm.session(prompt, N, W, G, n_new, ar=True)
+    ar_ses = gm.session(prompt, N, W, G, n_new, ar=True, debug_logits=True)
     ar_logits = []
     while not ar_ses.done:
-        ar_ses.step()
+        tok = ar_ses.step()
         ar_logits.append(ar_ses.logits(1)[0])
+        # the LM head's per-block argmax keys give the logits' argmax
+        # (ties to the lowest id)
+        row = ar_logits[-1]
+        assert tok[0] == int(np.flatnonzero(row == row.max())[0])
     ar_toks = ar_ses.tokens
     ar_ses.close()
     return s, w, gm, la_toks, ar_toks, np.array(ar_logits), st
@@ -450,3 +455,29 @@ def test_bf16_adaptive_g_bit_exact(name, N, W, G):
     for k in ("steps", "tokens", "inserts", "dup_skips", "evictions", "cand_total"):
         assert fixed[k] == adapt[k], k
     assert adapt["rows_total"] <= fixed["rows_total"] == fixed["steps"] * (1 + (W + G) * (N - 1))
+
+
+def test_bf16_argmax_ties_and_logits_on_demand():
+    """A zero LM head makes every logit 0: the argmax over the LM head's
+    per-block keys must take the lowest id, 0, at every row, so lookahead
+    and AR both emit only 0s.  A bf16 session keeps no logits unless asked
+    (LA_DEBUG_LOGITS); one that is asked returns them."""
+    s = synth.SHAPES["small_bf16"]
+    w = synth.gen_weights(s, 0)
+    w[-1] = np.zeros_like(w[-1])
+    gm = Model(s, w)
+    prompt = synth.prompt_zipf_spans(s.vocab, length=32, seed=3)
+    N, W, G = 4, 5, 5
+    la_ses = gm.session(prompt, N, W, G, 20, window=synth.gen_window(N, W, s.vocab, seed=2),
+                        prompt_ref=True)
+    assert la_ses.decode() == [0] * 20
+    with pytest.raises(B.LaError) as ei:
+        la_ses.logits()
+    assert ei.value.code == B.LA_ESTATE
+    la_ses.close()
+    ar = gm.session(prompt, N, W, G, 8, ar=True, debug_logits=True)
+    assert ar.step() == [0]
+    assert not ar.logits(1).any()
+    assert ar.decode() == [0] * 8
+    ar.close()
+    gm.close()

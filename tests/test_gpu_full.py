@@ -57,7 +57,7 @@ def _build(name):
 
 
 def _ar_logits(gm, prompt, n, N):
-    ses = gm.session(prompt, N, 0, 0, n, ar=True)
+    ses = gm.session(prompt, N, 0, 0, n, ar=True, debug_logits=True)
     lg = []
     while not ses.done:
         ses.step()

@@ -33,7 +33,8 @@ def test_flag_values_match_header():
     assert defs == {"LA_PROMPT_REF": str(B.LA_PROMPT_REF), "LA_AR": str(B.LA_AR),
                     "LA_NO_GRAPH": str(B.LA_NO_GRAPH), "LA_POOL_LRU": str(B.LA_POOL_LRU),
                     "LA_POOL_CONTEXT": str(B.LA_POOL_CONTEXT),
-                    "LA_ADAPTIVE_G": str(B.LA_ADAPTIVE_G)}
+                    "LA_ADAPTIVE_G": str(B.LA_ADAPTIVE_G),
+                    "LA_DEBUG_LOGITS": str(B.LA_DEBUG_LOGITS)}
 
 
 def _model(dtype=B.LA_BF16, L=2, d=512, H=4, Hkv=4, hd=128, F=1408, V=4000):
