@@ -315,3 +315,35 @@ def test_micro_sampling_pool_variants_match_oracle(micro, lru, ctx):
         compared += k
         ses.close()
     assert compared >= 24
+
+
+@pytest.mark.parametrize("graph", [True, False])
+def test_micro_sampling_adaptive_g_matches_oracle(micro, graph):
+    """Sampling verification in a LA_ADAPTIVE_G session: the candidate rows
+    left out are padding, so the draws (one per candidate tried) and every
+    decided token follow the oracle's fixed-G run; a fully decided run also
+    has the oracle's accepted-length histogram and pool counters."""
+    s, w, gm, om = micro
+    N, W, G, n_new, T = 3, 3, 6, 24, 0.7
+    compared = full = 0
+    for seed in range(6):
+        print(f"micro sampling adaptive G graph={graph} seed={seed}", flush=True)
+        win = synth.gen_window(N, W, s.vocab, seed=100 + seed)
+        ref = la.lookahead(om, MICRO_PROMPT, N, W, G, n_new, win, prompt_ref=True,
+                           temperature=T, seed=seed)
+        ses = gm.session(MICRO_PROMPT, N, W, G, n_new, window=win, prompt_ref=True,
+                         temperature=T, seed=seed, graph=graph, adaptive_g=True)
+        toks = ses.decode()
+        k = _decided_prefix(ref, ses.per_step, toks)
+        if k == len(ref.margins):
+            full += 1
+            assert toks == ref.tokens
+            st = ses.stats()
+            assert [st["accept_hist"][j] for j in range(N)] == \
+                [ref.accepted.count(j) for j in range(N)]
+            assert (st["inserts"], st["dup_skips"], st["evictions"]) == \
+                (ref.pool.inserts, ref.pool.dup_skips, ref.pool.evictions)
+            assert st["rows_total"] <= st["steps"] * (1 + (W + G) * (N - 1))
+        compared += k
+        ses.close()
+    assert compared >= 24 and full >= 1
