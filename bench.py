@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--top-p", type=float, default=0.0, help="sampling: top-P cut (0 = none)")
     ap.add_argument("--pool-lru", action="store_true",
                     help="evict pool n-grams by recency instead of FIFO (LA_POOL_LRU)")
+    ap.add_argument("--adaptive", choices=["on", "off"], default="on",
+                    help="also time the configuration with LA_ADAPTIVE_G (the adaptive_G field)")
     ap.add_argument("--pool-cap", type=int, default=0,
                     help="suffixes kept per first token (0 = G)")
     ap.add_argument("--pool-study", action="store_true",
@@ -632,7 +634,7 @@ def main():
     # rows only as far as its candidates need (every token, step and pool
     # counter as with the fixed width)
     adaptive = None
-    if args.temperature == 0:
+    if args.temperature == 0 and args.adaptive == "on":
         def la_adaptive():
             return model.session(prompt, N, W, G, args.max_new, window=window, prompt_ref=True,
                                  graph=graph, pool_cap=args.pool_cap, pool_lru=args.pool_lru,
