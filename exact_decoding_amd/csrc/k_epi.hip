@@ -278,9 +278,9 @@ hipError_t launch_qkv_epi(const QkvEpi& e, int dtype, hipStream_t st) {
     dim3 grid((units + 255) / 256, e.rows);
 #define LA_QKV4(S_)                                                             \
   if (dtype == LA_BF16)                                                         \
-    hipLaunchKernelGGL((k_qkv_epi4<bf16_t, S_>), grid, dim3(256), 0, st, e);    \
+    la_launch((k_qkv_epi4<bf16_t, S_>), grid, dim3(256), 0, st, e);             \
   else                                                                          \
-    hipLaunchKernelGGL((k_qkv_epi4<float, S_>), grid, dim3(256), 0, st, e);
+    la_launch((k_qkv_epi4<float, S_>), grid, dim3(256), 0, st, e);
     LA_SPLIT_DISPATCH(e.sp.np, LA_QKV4)
 #undef LA_QKV4
     return hipGetLastError();
@@ -289,9 +289,9 @@ hipError_t launch_qkv_epi(const QkvEpi& e, int dtype, hipStream_t st) {
   dim3 grid((units + 255) / 256, e.rows);
 #define LA_QKV(S_)                                                              \
   if (dtype == LA_BF16)                                                         \
-    hipLaunchKernelGGL((k_qkv_epi<bf16_t, S_>), grid, dim3(256), 0, st, e);     \
+    la_launch((k_qkv_epi<bf16_t, S_>), grid, dim3(256), 0, st, e);              \
   else                                                                          \
-    hipLaunchKernelGGL((k_qkv_epi<float, S_>), grid, dim3(256), 0, st, e);
+    la_launch((k_qkv_epi<float, S_>), grid, dim3(256), 0, st, e);
   LA_SPLIT_DISPATCH(e.sp.np, LA_QKV)
 #undef LA_QKV
   return hipGetLastError();
@@ -312,11 +312,11 @@ hipError_t launch_resid_norm(const float* part, const SplitPlan& sp, int rows_pa
     const dim3 blk(d / 4 / nc4);
 #define LA_RQ2(S_, NC_)                                                                        \
   if (dtype == LA_BF16)                                                                        \
-    hipLaunchKernelGGL((k_resid_norm4<bf16_t, S_, NC_>), dim3(rows), blk, 0, st, part, sp,     \
-                       rows_pad, d, x, (const bf16_t*)g, (bf16_t*)h, eps);                     \
+    la_launch((k_resid_norm4<bf16_t, S_, NC_>), dim3(rows), blk, 0, st, part, sp,              \
+              rows_pad, d, x, (const bf16_t*)g, (bf16_t*)h, eps);                              \
   else                                                                                         \
-    hipLaunchKernelGGL((k_resid_norm4<float, S_, NC_>), dim3(rows), blk, 0, st, part, sp,      \
-                       rows_pad, d, x, (const float*)g, (float*)h, eps);
+    la_launch((k_resid_norm4<float, S_, NC_>), dim3(rows), blk, 0, st, part, sp,               \
+              rows_pad, d, x, (const float*)g, (float*)h, eps);
 #define LA_RQ(S_)                                                       \
   switch (nc4) {                                                        \
     case 1: LA_RQ2(S_, 1) break;                                        \
@@ -335,11 +335,11 @@ hipError_t launch_resid_norm(const float* part, const SplitPlan& sp, int rows_pa
   const dim3 blk(d / nc);
 #define LA_RN2(S_, NC_)                                                                        \
   if (dtype == LA_BF16)                                                                        \
-    hipLaunchKernelGGL((k_resid_norm<bf16_t, S_, NC_>), dim3(rows), blk, 0, st, part, sp,      \
-                       rows_pad, d, x, (const bf16_t*)g, (bf16_t*)h, eps);                     \
+    la_launch((k_resid_norm<bf16_t, S_, NC_>), dim3(rows), blk, 0, st, part, sp,               \
+              rows_pad, d, x, (const bf16_t*)g, (bf16_t*)h, eps);                              \
   else                                                                                         \
-    hipLaunchKernelGGL((k_resid_norm<float, S_, NC_>), dim3(rows), blk, 0, st, part, sp,       \
-                       rows_pad, d, x, (const float*)g, (float*)h, eps);
+    la_launch((k_resid_norm<float, S_, NC_>), dim3(rows), blk, 0, st, part, sp,                \
+              rows_pad, d, x, (const float*)g, (float*)h, eps);
 #define LA_RN(S_)                                                       \
   switch (nc) {                                                         \
     case 1: LA_RN2(S_, 1) break;                                        \
@@ -359,8 +359,8 @@ hipError_t launch_resid_norm(const float* part, const SplitPlan& sp, int rows_pa
 hipError_t launch_sum_epi(const float* part, const SplitPlan& sp, int rows_pad, int N, int rows,
                           float* y, hipStream_t st) {
 #define LA_SE(S_)                                                                           \
-  hipLaunchKernelGGL((k_sum_epi<S_>), dim3((N + 255) / 256, rows), dim3(256), 0, st, part, sp, \
-                     rows_pad, N, y);
+  la_launch((k_sum_epi<S_>), dim3((N + 255) / 256, rows), dim3(256), 0, st, part, sp,       \
+            rows_pad, N, y);
   LA_SPLIT_DISPATCH(sp.np, LA_SE)
 #undef LA_SE
   return hipGetLastError();
@@ -372,22 +372,22 @@ hipError_t launch_silu_epi(const float* part, const SplitPlan& sp, int rows_pad,
     const dim3 grid((F / 4 + 255) / 256, rows);
 #define LA_SQ(S_)                                                                               \
   if (dtype == LA_BF16)                                                                         \
-    hipLaunchKernelGGL((k_silu_epi4<bf16_t, S_>), grid, dim3(256), 0, st, part, sp, rows_pad,  \
-                       F, (bf16_t*)act);                                                        \
+    la_launch((k_silu_epi4<bf16_t, S_>), grid, dim3(256), 0, st, part, sp, rows_pad,            \
+              F, (bf16_t*)act);                                                                 \
   else                                                                                          \
-    hipLaunchKernelGGL((k_silu_epi4<float, S_>), grid, dim3(256), 0, st, part, sp, rows_pad,   \
-                       F, (float*)act);
+    la_launch((k_silu_epi4<float, S_>), grid, dim3(256), 0, st, part, sp, rows_pad,             \
+              F, (float*)act);
     LA_SPLIT_DISPATCH(sp.np, LA_SQ)
 #undef LA_SQ
     return hipGetLastError();
   }
 #define LA_SI(S_)                                                                              \
   if (dtype == LA_BF16)                                                                        \
-    hipLaunchKernelGGL((k_silu_epi<bf16_t, S_>), dim3((F + 255) / 256, rows), dim3(256), 0, st, \
-                       part, sp, rows_pad, F, (bf16_t*)act);                                   \
+    la_launch((k_silu_epi<bf16_t, S_>), dim3((F + 255) / 256, rows), dim3(256), 0, st,         \
+              part, sp, rows_pad, F, (bf16_t*)act);                                            \
   else                                                                                         \
-    hipLaunchKernelGGL((k_silu_epi<float, S_>), dim3((F + 255) / 256, rows), dim3(256), 0, st,  \
-                       part, sp, rows_pad, F, (float*)act);
+    la_launch((k_silu_epi<float, S_>), dim3((F + 255) / 256, rows), dim3(256), 0, st,          \
+              part, sp, rows_pad, F, (float*)act);
   LA_SPLIT_DISPATCH(sp.np, LA_SI)
 #undef LA_SI
   return hipGetLastError();

@@ -617,8 +617,8 @@ __global__ __launch_bounds__(128) void k_pack_bf16(const bf16_t* __restrict__ sr
 size_t packed_bytes(int N, int K) { return (size_t)((N + 15) / 16) * 16 * K * 2; }
 
 hipError_t launch_pack(const void* src, int N, int K, void* dst, hipStream_t st) {
-  hipLaunchKernelGGL(k_pack_bf16, dim3(K / KC, (N + 15) / 16), dim3(128), 0, st,
-                     (const bf16_t*)src, N, K, (bf16_t*)dst);
+  la_launch(k_pack_bf16, dim3(K / KC, (N + 15) / 16), dim3(128), 0, st,
+            (const bf16_t*)src, N, K, (bf16_t*)dst);
   return hipGetLastError();
 }
 
@@ -662,7 +662,7 @@ SplitPlan gemm_plan(int N, int K, int dtype) {
 hipError_t launch_gemm(const GemmDesc& g, int dtype, hipStream_t st) {
   if (dtype == LA_F32) {
     dim3 grid((g.N + 63) / 64, g.rows);
-    hipLaunchKernelGGL(k_gemm_f32, grid, dim3(64), 0, st, g);
+    la_launch(k_gemm_f32, grid, dim3(64), 0, st, g);
     return hipGetLastError();
   }
   if (g.sp.nblk != (g.N + NWG - 1) / NWG || g.sp.nch != g.K / KC) return hipErrorInvalidValue;
@@ -681,14 +681,14 @@ hipError_t launch_gemm(const GemmDesc& g, int dtype, hipStream_t st) {
   // the same MFMA order, so a row's sums do not depend on which one ran.
   const dim3 b4(256);
   switch (mt) {
-    case 1: hipLaunchKernelGGL(k_gemm_bf16<1>, grid, dim3(320), 0, st, g); break;
-    case 2: hipLaunchKernelGGL(k_gemm4<2>, grid, b4, 0, st, g); break;
-    case 3: hipLaunchKernelGGL(k_gemm4<3>, grid, b4, 0, st, g); break;
-    case 4: hipLaunchKernelGGL(k_gemm4<4>, grid, b4, 0, st, g); break;
-    case 5: hipLaunchKernelGGL(k_gemm4<5>, grid, b4, 0, st, g); break;
-    case 6: hipLaunchKernelGGL(k_gemm4<6>, grid, b4, 0, st, g); break;
-    case 7: hipLaunchKernelGGL(k_gemm4<7>, grid, b4, 0, st, g); break;
-    default: hipLaunchKernelGGL(k_gemm4<8>, grid, b4, 0, st, g); break;
+    case 1: la_launch(k_gemm_bf16<1>, grid, dim3(320), 0, st, g); break;
+    case 2: la_launch(k_gemm4<2>, grid, b4, 0, st, g); break;
+    case 3: la_launch(k_gemm4<3>, grid, b4, 0, st, g); break;
+    case 4: la_launch(k_gemm4<4>, grid, b4, 0, st, g); break;
+    case 5: la_launch(k_gemm4<5>, grid, b4, 0, st, g); break;
+    case 6: la_launch(k_gemm4<6>, grid, b4, 0, st, g); break;
+    case 7: la_launch(k_gemm4<7>, grid, b4, 0, st, g); break;
+    default: la_launch(k_gemm4<8>, grid, b4, 0, st, g); break;
   }
   return hipGetLastError();
 }

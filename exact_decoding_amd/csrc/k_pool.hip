@@ -744,58 +744,58 @@ __global__ __launch_bounds__(256) void k_probe_read(const uint4* __restrict__ bu
 }  // namespace
 
 hipError_t launch_probe_read(const void* buf, size_t bytes, uint32_t* out, hipStream_t st) {
-  hipLaunchKernelGGL(k_probe_read, dim3(LA_PROBE_BLOCKS), dim3(256), 0, st, (const uint4*)buf, bytes / 16,
-                     out);
+  la_launch(k_probe_read, dim3(LA_PROBE_BLOCKS), dim3(256), 0, st, (const uint4*)buf, bytes / 16,
+            out);
   return hipGetLastError();
 }
 
 hipError_t launch_gather(const PoolDesc& pool, const StepIO& io, const RowLayout& lay,
                          hipStream_t st) {
   if (lay.G > GATHER_MAX_G) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_gather, dim3(1), dim3(256), 0, st, pool, io, lay);
+  la_launch(k_gather, dim3(1), dim3(256), 0, st, pool, io, lay);
   return hipGetLastError();
 }
 
 hipError_t launch_verify(const PoolDesc& pool, const StepIO& io, const RowLayout& lay,
                          hipStream_t st) {
   if (lay.M > VMAX_M || lay.G > 1024) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_verify, dim3(1), dim3(VFY_T), 0, st, pool, io, lay);
+  la_launch(k_verify, dim3(1), dim3(VFY_T), 0, st, pool, io, lay);
   return hipGetLastError();
 }
 
 hipError_t launch_sample_verify(const StepIO& io, const RowLayout& lay, hipStream_t st) {
   if (lay.M > VMAX_M || io.V > SAMPLE_VMAX || io.V < 1 || !(io.temp > 0.f))
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_sample_verify, dim3(1), dim3(SV_T), 0, st, io, lay);
+  la_launch(k_sample_verify, dim3(1), dim3(SV_T), 0, st, io, lay);
   return hipGetLastError();
 }
 
 hipError_t launch_philox_uniform(unsigned long long seed, unsigned long long step, int n,
                                  float* out, hipStream_t st) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_philox_uniform, dim3((n + 255) / 256), dim3(256), 0, st, seed, step, n,
-                     out);
+  la_launch(k_philox_uniform, dim3((n + 255) / 256), dim3(256), 0, st, seed, step, n,
+            out);
   return hipGetLastError();
 }
 
 hipError_t launch_kv_commit(const KvCommit& c, int dtype, hipStream_t st) {
   dim3 grid(c.L, c.nmax);
   if (dtype == LA_BF16)
-    hipLaunchKernelGGL(k_kv_commit<bf16_t>, grid, dim3(256), 0, st, c);
+    la_launch(k_kv_commit<bf16_t>, grid, dim3(256), 0, st, c);
   else
-    hipLaunchKernelGGL(k_kv_commit<float>, grid, dim3(256), 0, st, c);
+    la_launch(k_kv_commit<float>, grid, dim3(256), 0, st, c);
   return hipGetLastError();
 }
 
 hipError_t launch_pool_seed(const PoolDesc& pool, DevState* st, const int32_t* prompt, int n,
                             hipStream_t st_) {
-  hipLaunchKernelGGL(k_pool_seed, dim3(1), dim3(64), 0, st_, pool, st, prompt, n);
+  la_launch(k_pool_seed, dim3(1), dim3(64), 0, st_, pool, st, prompt, n);
   return hipGetLastError();
 }
 
 hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t st) {
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_fill_i32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, v, n);
+  la_launch(k_fill_i32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, v, n);
   return hipGetLastError();
 }
 

@@ -273,6 +273,11 @@ struct la_session {
   T* at(size_t off) const { return (T*)(base + off); }
 };
 
+KernelTimer& kernel_timer() {
+  static thread_local KernelTimer t;
+  return t;
+}
+
 namespace {
 
 // Whether every step leaves the logits in the workspace (la_debug_logits).
@@ -300,21 +305,28 @@ hipError_t launch_checked(hipError_t e, const char* what, hipStream_t st) {
       return fail(LA_EHIP, std::string(what) + ": " + hipGetErrorString(e_));     \
   } while (0)
 
-// LA_K with the launch bracketed by hipEvents when the session profiles.
+// LA_K with the kernels of the launch timed by events bound to them when the
+// session profiles (KernelTimer); a launch that ran no kernel is not counted.
 #define LA_KP(kind, bytes, flops, expr, what)                                     \
   do {                                                                            \
-    hipEvent_t a_ = nullptr, b_ = nullptr;                                        \
+    KernelTimer& kt_ = kernel_timer();                                            \
     if (ss->prof_on) {                                                            \
-      a_ = ss->next_event();                                                      \
-      b_ = ss->next_event();                                                      \
-      if (!a_ || !b_) return fail(LA_EHIP, "hipEventCreate failed");              \
-      LA_K(hipEventRecord(a_, st), "event");                                      \
+      kt_.start = ss->next_event();                                               \
+      kt_.stop = ss->next_event();                                                \
+      kt_.started = false;                                                        \
+      if (!kt_.start || !kt_.stop) {                                              \
+        kt_ = KernelTimer{};                                                      \
+        return fail(LA_EHIP, "hipEventCreate failed");                            \
+      }                                                                           \
     }                                                                             \
-    LA_K(expr, what);                                                             \
-    if (ss->prof_on) {                                                            \
-      LA_K(hipEventRecord(b_, st), "event");                                      \
+    const hipEvent_t a_ = kt_.start, b_ = kt_.stop;                               \
+    const hipError_t e_ = launch_checked((expr), what, st);                       \
+    const bool timed_ = kt_.started;                                              \
+    kt_ = KernelTimer{};                                                          \
+    if (e_ != hipSuccess)                                                         \
+      return fail(LA_EHIP, std::string(what) + ": " + hipGetErrorString(e_));     \
+    if (ss->prof_on && timed_)                                                    \
       ss->recs.push_back({kind, a_, b_, (double)(bytes), (double)(flops)});       \
-    }                                                                             \
   } while (0)
 
 // la_step_trace: append `bytes` from device memory `src` to the trace.

@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 
 #include "la.h"
@@ -27,6 +28,33 @@ __device__ __forceinline__ bf16_t f2bf(float f) {
 }
 __device__ __forceinline__ void st_f(float* p, float v) { *p = v; }
 __device__ __forceinline__ void st_f(bf16_t* p, float v) { *p = f2bf(v); }
+
+// ---------------------------------------------------------------------------
+// kernel launches, with optional per-kernel timing (la_step_profile)
+// ---------------------------------------------------------------------------
+// While `stop` is set on the calling thread, launches through la_launch bind
+// the events to the kernels' own start and end (hipExtLaunchKernelGGL):
+// `start` to the first kernel launched, `stop` to the last one, so the
+// elapsed time between them is what the kernels took on the device, without
+// the gaps that event records between eager launches would add.
+struct KernelTimer {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+  bool started = false;
+};
+KernelTimer& kernel_timer();  // the calling thread's
+
+template <typename F, typename... A>
+inline void la_launch(F kernel, dim3 grid, dim3 block, uint32_t shmem, hipStream_t st, A... args) {
+  KernelTimer& t = kernel_timer();
+  if (t.stop) {
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, t.started ? nullptr : t.start, t.stop, 0,
+                          args...);
+    t.started = true;
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, shmem, st, args...);
+  }
+}
 
 // ---------------------------------------------------------------------------
 // device-resident decoding state (one per session, in the workspace)

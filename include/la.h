@@ -230,14 +230,15 @@ enum {
 };
 typedef struct {
   int32_t launches[LA_PROF_KINDS];
-  double ms[LA_PROF_KINDS];     /* summed hipEvent intervals              */
+  double ms[LA_PROF_KINDS];     /* summed kernel durations (device clock) */
   double bytes[LA_PROF_KINDS];  /* algorithmic HBM bytes of those launches */
   double flops[LA_PROF_KINDS];  /* algorithmic FLOPs of those launches     */
 } la_profile_t;
 
-/* la_step with every kernel launched eagerly and bracketed by a pair of
- * hipEvents on the session's stream; *prof receives the per-class sums.
- * Same kernels, grids and arguments as the graph replay.  Algorithmic bytes:
+/* la_step with every kernel launched eagerly, each launch's kernels timed by
+ * a pair of hipEvents bound to their own start and end (hipExtLaunchKernel),
+ * so gaps between launches are not counted; *prof receives the per-class
+ * sums.  Same kernels, grids and arguments as the graph replay.  Algorithmic bytes:
  * GEMM = weights + input rows + fp32 output rows; attention = committed K/V
  * read once per KV head + block K/V + q + output. */
 int la_step_profile(la_session* s, int32_t* out_tokens, int32_t out_cap, int32_t* n_out,

@@ -481,3 +481,36 @@ def test_bf16_argmax_ties_and_logits_on_demand():
     assert ar.decode() == [0] * 8
     ar.close()
     gm.close()
+
+
+def test_bf16_step_profile_counts_and_tokens():
+    """la_step_profile runs the step eagerly with every launch timed on the
+    device: its tokens equal la_step's, each launch class is counted once
+    per launch (four projections, one attention and four epilogues per
+    layer; embed and first norm; LM head; argmax; gather, verify, commit),
+    every class has a positive time, and the classes together take less
+    than the call's wall time."""
+    import time
+    s = synth.SHAPES["small_bf16"]
+    gm = Model(s, synth.gen_weights(s, 0))
+    prompt = synth.prompt_zipf_spans(s.vocab, length=48, seed=4)
+    N, W, G = 5, 7, 7
+    win = synth.gen_window(N, W, s.vocab, seed=2)
+    ref = gm.session(prompt, N, W, G, 24, window=win, prompt_ref=True)
+    ref_toks = ref.decode()
+    ref.close()
+    ses = gm.session(prompt, N, W, G, 24, window=win, prompt_ref=True)
+    L = s.n_layers
+    want = {"gemm": 4 * L, "lm_head": 1, "attention": L, "norm": 2, "epilogue": 4 * L,
+            "argmax": 1, "bookkeeping": 3}
+    while not ses.done:
+        t0 = time.perf_counter()
+        _, prof = ses.step_profile()
+        wall_ms = (time.perf_counter() - t0) * 1e3
+        for k, n in want.items():
+            assert prof[k]["launches"] == n, (k, prof[k])
+            assert prof[k]["ms"] > 0, (k, prof[k])
+        assert sum(v["ms"] for v in prof.values()) < wall_ms
+    assert ses.tokens == ref_toks
+    ses.close()
+    gm.close()
