@@ -561,35 +561,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // 32 dims of one key of K and 16 dims of a key pair of V, fetched one tile
   // ahead so the loads of tile t+1 overlap the arithmetic of tile t.  Keys
   // at or past tend (past every row's MFMA part, possibly never written)
-  // are staged as zeros: masked rows then add exactly 0 * 0.
+  // are staged as zeros: masked rows then add exactly 0 * 0.  The loaded
+  // words are only selected at the LDS store, so nothing waits for the
+  // loads before the tile's arithmetic.
   const int fkey = tid >> 2, fseg = tid & 3;  // K: 32 dims per thread
   const int fkp = tid & 31, fvs = tid >> 5;   // V: key pair, 16-dim segment
-  u32x4_t kf[4];
-  U4 va0, va1, vb0, vb1;
+  u32x4_t kf[4], va[2], vb[2];
+  bool kok = false, v0ok = false, v1ok = false;
   const u32x4_t z4 = u32x4_t{0u, 0u, 0u, 0u};
   auto fetch = [&](int t0) __attribute__((always_inline)) {
     // addresses clamped to key tend-1 (a tile may reach past the cache's
-    // capacity); the loaded words of such keys are replaced by zeros
+    // capacity); the words of such keys are replaced by zeros at the store
     const int k0 = t0 + fkey, v0k = t0 + 2 * fkp;
     const int kl = min(k0, tend - 1), v0l = min(v0k, tend - 1), v1l = min(v0k + 1, tend - 1);
     const u32x4_t* src = (const u32x4_t*)(kc + (size_t)kl * 128 + fseg * 32);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const u32x4_t w = src[j];
-      kf[j] = k0 < tend ? w : z4;
-    }
+    for (int j = 0; j < 4; ++j) kf[j] = src[j];
     const u32x4_t* v0 = (const u32x4_t*)(vc + (size_t)v0l * 128 + fvs * 16);
     const u32x4_t* v1 = (const u32x4_t*)(vc + (size_t)v1l * 128 + fvs * 16);
-    const u32x4_t a0 = v0[0], a1 = v0[1], b0 = v1[0], b1 = v1[1];
-    va0.u = v0k < tend ? a0 : z4;
-    va1.u = v0k < tend ? a1 : z4;
-    vb0.u = v0k + 1 < tend ? b0 : z4;
-    vb1.u = v0k + 1 < tend ? b1 : z4;
+    va[0] = v0[0];
+    va[1] = v0[1];
+    vb[0] = v1[0];
+    vb[1] = v1[1];
+    kok = k0 < tend;
+    v0ok = v0k < tend;
+    v1ok = v0k + 1 < tend;
   };
   fetch(s0);
   for (int t0 = s0; t0 < tend; t0 += AT) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) *(u32x4_t*)(&Ks[fkey * KSTR + fseg * 32 + j * 8]) = kf[j];
+    for (int j = 0; j < 4; ++j) *(u32x4_t*)(&Ks[fkey * KSTR + fseg * 32 + j * 8]) = kok ? kf[j] : z4;
+    U4 va0, va1, vb0, vb1;
+    va0.u = v0ok ? va[0] : z4;
+    va1.u = v0ok ? va[1] : z4;
+    vb0.u = v1ok ? vb[0] : z4;
+    vb1.u = v1ok ? vb[1] : z4;
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
       *(uint32_t*)(&Vt[(fvs * 16 + d) * VSTR + 2 * fkp]) =
@@ -760,7 +766,7 @@ __global__ __launch_bounds__(64) void k_argmax_keys(const unsigned long long* ke
 
 hipError_t launch_argmax_keys(const unsigned long long* keys, int rows, int nblk, int32_t* out,
                               hipStream_t st) {
-  hipLaunchKernelGGL(k_argmax_keys, dim3(rows), dim3(64), 0, st, keys, nblk, out);
+  la_launch(k_argmax_keys, dim3(rows), dim3(64), 0, st, keys, nblk, out);
   return hipGetLastError();
 }
 
@@ -775,16 +781,15 @@ hipError_t launch_attention(const AttnDesc& a, int dtype, hipStream_t st) {
   if (a.mfma) {
     if (dtype != LA_BF16 || a.hd != 128 || a.nsplit < 1)
       return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_attn_bulk, dim3(a.H, a.nsplit, (a.rows + 127) / 128), dim3(256), 0, st,
-                       a);
+    la_launch(k_attn_bulk, dim3(a.H, a.nsplit, (a.rows + 127) / 128), dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_attn_tail<bf16_t, 128>), grid, dim3(64), 0, st, a);
+    la_launch((k_attn_tail<bf16_t, 128>), grid, dim3(64), 0, st, a);
     return hipGetLastError();
   }
 #define LA_ATTN_CASE(T, HD)                                                  \
   if (a.hd == HD) {                                                          \
-    hipLaunchKernelGGL((k_attn_tail<T, HD>), grid, dim3(64), 0, st, a);      \
+    la_launch((k_attn_tail<T, HD>), grid, dim3(64), 0, st, a);               \
     return hipGetLastError();                                                \
   }
   if (dtype == LA_BF16) {
@@ -805,28 +810,27 @@ hipError_t launch_attention(const AttnDesc& a, int dtype, hipStream_t st) {
 hipError_t launch_rmsnorm(const float* x, const void* g, void* y, int rows, int d, float eps,
                           int dtype, hipStream_t st) {
   if (dtype == LA_BF16)
-    hipLaunchKernelGGL(k_rmsnorm<bf16_t>, dim3(rows), dim3(256), 0, st, x, (const bf16_t*)g,
-                       (bf16_t*)y, d, eps);
+    la_launch(k_rmsnorm<bf16_t>, dim3(rows), dim3(256), 0, st, x, (const bf16_t*)g,
+              (bf16_t*)y, d, eps);
   else
-    hipLaunchKernelGGL(k_rmsnorm<float>, dim3(rows), dim3(256), 0, st, x, (const float*)g,
-                       (float*)y, d, eps);
+    la_launch(k_rmsnorm<float>, dim3(rows), dim3(256), 0, st, x, (const float*)g,
+              (float*)y, d, eps);
   return hipGetLastError();
 }
 
 hipError_t launch_embed(const int32_t* ids, const void* emb, float* x, int rows, int d, int dtype,
                         hipStream_t st) {
   if (dtype == LA_BF16)
-    hipLaunchKernelGGL(k_embed<bf16_t>, dim3(rows), dim3(256), 0, st, ids, (const bf16_t*)emb, x,
-                       d);
+    la_launch(k_embed<bf16_t>, dim3(rows), dim3(256), 0, st, ids, (const bf16_t*)emb, x, d);
   else
-    hipLaunchKernelGGL(k_embed<float>, dim3(rows), dim3(256), 0, st, ids, (const float*)emb, x, d);
+    la_launch(k_embed<float>, dim3(rows), dim3(256), 0, st, ids, (const float*)emb, x, d);
   return hipGetLastError();
 }
 
 hipError_t launch_argmax(const float* logits, int rows, int V, int32_t* out, hipStream_t st) {
   if (V % 4 == 0)
-    hipLaunchKernelGGL(k_argmax<true>, dim3(rows), dim3(1024), 0, st, logits, V, out);
+    la_launch(k_argmax<true>, dim3(rows), dim3(1024), 0, st, logits, V, out);
   else
-    hipLaunchKernelGGL(k_argmax<false>, dim3(rows), dim3(1024), 0, st, logits, V, out);
+    la_launch(k_argmax<false>, dim3(rows), dim3(1024), 0, st, logits, V, out);
   return hipGetLastError();
 }
