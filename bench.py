@@ -312,11 +312,38 @@ def sweep(args, model, shape, prompt):
     return {"rows": table, "ar_ms": ar_ms}
 
 
-def attention_bench(read_gbps):
+def attention_cpu_leg(bufs, out, P, N, W, G, H, hd):
+    """The oracle's attention (float64 numpy, the lookahead mask
+    materialised) on the same call's inputs: its time per call on the host,
+    and the largest difference of the GPU's bf16 output from it."""
+    import numpy as np
+    import torch
+    from oracle.attention import lookahead_attention
+    q, kc, vc, kb, vb = (t.float().cpu().numpy() for t in bufs)
+    M = q.shape[0]
+    args = (q.reshape(M, H, hd), kc[:, :P].transpose(1, 0, 2), vc[:, :P].transpose(1, 0, 2),
+            kb.reshape(M, H, hd), vb.reshape(M, H, hd), N, W, G)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        ref = lookahead_attention(*args)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt > 1.0 or reps == 3:
+            break
+    err = float(np.abs(out.float().cpu().numpy().reshape(M, H, hd) - ref).max())
+    return {"value": dt / reps * 1e6, "unit": "us per call", "cores": min(blas_threads(), host_cpu()[1]),
+            "kind": "oracle", "sample": f"the same call (P = {P}, {M} rows, {H} heads), float64 numpy "
+                                        f"with the mask materialised, {reps} call(s)",
+            "gpu_max_abs_err": err}
+
+
+def attention_bench(read_gbps, cpu_leg=True):
     """The attention call alone (both kernels) on seeded N(0, 1) bf16 data,
     rotating over enough buffer sets that the K/V working set exceeds the
     256 MB memory-side cache; bytes per call = the prefix K and V plus q,
-    block K/V and the output."""
+    block K/V and the output.  With `cpu_leg`, each line also carries the
+    oracle's time for the same call and the GPU output's largest error
+    against it."""
     import torch
     from exact_decoding_amd import binding as B
     H, hd = 32, 128
@@ -353,11 +380,16 @@ def attention_bench(read_gbps):
             us = e0.elapsed_time(e1) / it * 1e3
             nbytes = 16384 * P + 4 * M * H * hd * 2
             gbps = nbytes / (us * 1e-6) / 1e9
+            cpu = None
+            if cpu_leg:
+                run(0)
+                torch.cuda.synchronize()
+                cpu = attention_cpu_leg(sets[0], out, P, N, W, G, H, hd)
             print(json.dumps({"kernel": "lookahead attention (MFMA prefix part + per-row part)",
                               "P": P, "N": N, "W": W, "G": G, "rows": M, "us_per_call": us,
                               "bytes_per_call": nbytes, "GBps": gbps, "frac": gbps / HBM_PEAK_GBPS,
                               "frac_of_achievable": gbps / read_gbps if read_gbps else None,
-                              "buffer_sets": nset}), flush=True)
+                              "buffer_sets": nset, "cpu_baseline": cpu}), flush=True)
             del sets, out, ws
             torch.cuda.empty_cache()
 
@@ -543,7 +575,7 @@ def main():
         read_gbps = calibrate()
         log(f"[bench] calibration: 1 GiB read at {read_gbps:.0f} GB/s")
     if args.attention:
-        attention_bench(read_gbps)
+        attention_bench(read_gbps, cpu_leg=args.cpu_baseline == "on")
         return
     if args.gemm:
         gemm_bench(shape, 1 + (W + G) * (N - 1), read_gbps)
