@@ -332,9 +332,10 @@ __global__ __launch_bounds__(64) void k_attn_tail(AttnDesc a) {
 }
 
 // MFMA part (bf16, head_dim 128): one workgroup per (head, prefix chunk
-// committed positions, block of 128 rows).  Each 64-position tile of K and V
-// is staged in LDS once and used by every row; wave w handles the 16-row
-// groups w and w+4, both on each tile (group_tiles<2>).
+// committed positions, block of 64 or 128 rows).  Each 64-position tile of
+// K and V is staged in LDS once and used by every row of the block; wave w
+// handles the 16-row group w, or with 128 rows the groups w and w+4, both on
+// each tile (group_tiles<2>).
 //
 // Scores are computed transposed, S^T = K Q^T (v_mfma_f32_16x16x32_bf16,
 // A = 16 keys x 32 dims of K, B = 32 dims x 16 rows of Q^T), so a lane holds
@@ -345,6 +346,7 @@ __global__ __launch_bounds__(64) void k_attn_tail(AttnDesc a) {
 // 32j + 16 + 4(lane/16) + s - 4, and V is read transposed from LDS with the
 // same key order.  A tile that lies past a row's bulk end leaves that row's
 // state unchanged (alpha = 1, p = 0).
+constexpr int ATT_WIDE_P = 1024;  // committed length from which a workgroup takes 128 rows
 constexpr int KSTR = 128 + 8;  // LDS row stride of K (bf16)
 constexpr int VSTR = AT + 8;   // LDS row stride of V^T (bf16)
 
@@ -521,8 +523,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int c16 = lane & 15, q4 = lane >> 4;
   const int kvh = h * a.Hkv / a.H;
   const int Pc = a.Pdev ? *a.Pdev : a.P_host;
-  const int row0 = rb * 128;
-  const int nrows = min(128, a.rows - row0);
+  // The grid has one z index per 64 rows.  Below ATT_WIDE_P committed
+  // positions (few chunks, one or two tiles each) each workgroup takes its
+  // 64 rows, one 16-row group per wave, so twice as many workgroups share
+  // the work; from ATT_WIDE_P on, even z indices take 128 rows (two groups
+  // per wave, each K/V tile serving both) and odd ones have nothing to do.
+  // A row's arithmetic is the same either way (group_tiles<1> and <2>).
+  const bool wide = Pc >= ATT_WIDE_P;
+  if (wide && (rb & 1)) return;
+  const int row0 = rb * 64;
+  const int nrows = min(wide ? 128 : 64, a.rows - row0);
   const int ngroups = (nrows + 15) >> 4;
   const int s0 = attn_chunk_start(split);
   const bf16_t* kc = (const bf16_t*)a.kc + (size_t)kvh * a.ld_ctx * 128;
@@ -781,7 +791,7 @@ hipError_t launch_attention(const AttnDesc& a, int dtype, hipStream_t st) {
   if (a.mfma) {
     if (dtype != LA_BF16 || a.hd != 128 || a.nsplit < 1)
       return hipErrorInvalidValue;
-    la_launch(k_attn_bulk, dim3(a.H, a.nsplit, (a.rows + 127) / 128), dim3(256), 0, st, a);
+    la_launch(k_attn_bulk, dim3(a.H, a.nsplit, (a.rows + 63) / 64), dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     la_launch((k_attn_tail<bf16_t, 128>), grid, dim3(64), 0, st, a);

@@ -156,14 +156,16 @@ def test_attention_matches_oracle(P, H, Hkv, hd, N, W, G, dtype):
 
 @pytest.mark.parametrize("P,W,G", [(5, 3, 3), (63, 3, 3), (64, 3, 3), (130, 3, 3), (300, 3, 3),
                                    (525, 3, 3), (1100, 3, 3), (130, 15, 15), (300, 15, 15),
-                                   (525, 15, 15), (1100, 15, 15)])
+                                   (525, 15, 15), (1100, 15, 15), (300, 20, 20), (1100, 20, 20)])
 def test_attention_verification_row_equals_ar_query(P, W, G):
     """Verification row (g, i) == one query at P+i over a cache holding the
     prefix and the row's chain (what an autoregressive step computes).
-    With W = G = 3 (25 rows) each wave of the MFMA prefix part holds one
-    16-row group, as the single query does; with W = G = 15 (121 rows) every
-    wave holds two groups and runs them together on each tile, so the rows
-    go through the two-group path and the query through the one-group path."""
+    Below 1024 committed positions each wave of the MFMA prefix part holds
+    one 16-row group of a 64-row block, as the single query does; from 1024
+    on a workgroup takes 128 rows and every wave runs two groups together on
+    each tile (W = G = 15: 121 rows; W = G = 20: 161 rows, a 128-row block
+    and a 33-row one), so the rows go through the two-group path and the
+    query through the one-group path."""
     H, Hkv, hd, N = 4, 4, 128, 5
     M, ld, dev, host, tdt = _rand_attn(P, H, Hkv, hd, N, W, G, B.LA_BF16, seed=P, ld_ctx=P + 16)
     out = _run_attn(dev, P, ld, H, Hkv, hd, N, W, G, B.LA_BF16, tdt, M)
