@@ -344,30 +344,33 @@ __global__ void k_philox_uniform(unsigned long long seed, unsigned long long ste
 
 constexpr int SV_T = 1024;  // threads of the sampling verification
 
-// One workgroup.  e[v] = exp((logit_v - max) / T) of the current row lives in
-// LDS; thread t owns the contiguous vocabulary slice [t*CH, (t+1)*CH).
-// Sums: each thread adds its slice in index order; the 1024 slice sums are
-// added by a fixed halving tree (Z) or scanned (wave scans by shuffles, then
-// the 16 wave totals in order) for the residual draw.
-__global__ __launch_bounds__(SV_T) void k_sample_verify(StepIO io, RowLayout L) {
-  __shared__ float e[SAMPLE_VMAX];
+// Sampling weights of the rows the verification may visit: row 0 and every
+// verification row of a gathered candidate, one workgroup each, all at once
+// (they depend on their row's logits only).  Block b takes row 0 (b = 0) or
+// verification row b - 1; it leaves e[v] = exp((logit_v - max) / T), cut to
+// the top-K / top-P set, in sw[b][v] and their sum Z in sz[b].  Thread t
+// owns the contiguous vocabulary slice [t*CH, (t+1)*CH).  Sums: each thread
+// adds its slice in index order; the 1024 slice sums are added by a fixed
+// halving tree (Z) or scanned (wave scans by shuffles, then the 16 wave
+// totals in order).
+__global__ __launch_bounds__(SV_T) void k_sample_weights(StepIO io, RowLayout L) {
+  __shared__ __align__(16) float e[SAMPLE_VMAX];
   __shared__ float red[SV_T];
-  __shared__ float wtot[SV_T / 64];
-  __shared__ int wcnt[SV_T / 64];
-  __shared__ int32_t removed[VMAX_M];
-  __shared__ int32_t surv[VMAX_M];
-  __shared__ int s_nrem, s_pick, s_nsurv, s_row, s_done_pos;
-  __shared__ float s_target;
-  __shared__ int32_t emitted[LA_MAX_N];  // accepted tokens, then the drawn one
-  DevState* st = io.st;
+  // wave totals, double-buffered: a reduction writes the buffer the one
+  // before it did not, so one barrier per reduction suffices (every thread
+  // has read a buffer before it passes the next reduction's barrier)
+  __shared__ float wtot[2][SV_T / 64];
+  __shared__ int wcnt[2][SV_T / 64];
+  int par = 0;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int n1 = L.N - 1, V = io.V;
-  const int vbase = 1 + L.W * n1;
+  const int b = blockIdx.x;
+  // a verification row of a candidate the gather did not fill is never visited
+  if (b > 0 && (b - 1) / n1 >= io.st->ncand) return;
+  const int row = b == 0 ? 0 : 1 + L.W * n1 + (b - 1);
   const int CH = (V + SV_T - 1) / SV_T;
   const int v0 = min(V, tid * CH), v1 = min(V, v0 + CH);
-  const unsigned long long step = (unsigned long long)st->stats[ST_STEPS];
-  const int ncand = st->ncand;
-  uint32_t k = 0;  // draws used (same on every thread)
+  constexpr int CHMAX = (SAMPLE_VMAX + SV_T - 1) / SV_T;
 
   // Block-wide integer count and float sum, the same on every thread: a
   // shuffle tree within each wave (each pairwise sum is symmetric, so every
@@ -375,21 +378,21 @@ __global__ __launch_bounds__(SV_T) void k_sample_verify(StepIO io, RowLayout L) 
   auto block_count = [&](int c) -> int {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
-    if (lane == 0) wcnt[wv] = c;
+    if (lane == 0) wcnt[par][wv] = c;
     __syncthreads();
     int t = 0;
-    for (int w = 0; w < SV_T / 64; ++w) t += wcnt[w];
-    __syncthreads();
+    for (int w = 0; w < SV_T / 64; ++w) t += wcnt[par][w];
+    par ^= 1;
     return t;
   };
   auto block_fsum = [&](float x) -> float {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
-    if (lane == 0) wtot[wv] = x;
+    if (lane == 0) wtot[par][wv] = x;
     __syncthreads();
     float t = 0.f;
-    for (int w = 0; w < SV_T / 64; ++w) t += wtot[w];
-    __syncthreads();
+    for (int w = 0; w < SV_T / 64; ++w) t += wtot[par][w];
+    par ^= 1;
     return t;
   };
   // exclusive prefix over the threads (vocabulary order) of x
@@ -400,11 +403,11 @@ __global__ __launch_bounds__(SV_T) void k_sample_verify(StepIO io, RowLayout L) 
       const float t = __shfl_up(y, o, 64);
       if (lane >= o) y += t;
     }
-    if (lane == 63) wtot[wv] = y;
+    if (lane == 63) wtot[par][wv] = y;
     __syncthreads();
     float before = 0.f;
-    for (int w = 0; w < wv; ++w) before += wtot[w];
-    __syncthreads();
+    for (int w = 0; w < wv; ++w) before += wtot[par][w];
+    par ^= 1;
     return before + (y - x);
   };
   auto block_exscan_i = [&](int x) -> int {
@@ -414,11 +417,11 @@ __global__ __launch_bounds__(SV_T) void k_sample_verify(StepIO io, RowLayout L) 
       const int t = __shfl_up(y, o, 64);
       if (lane >= o) y += t;
     }
-    if (lane == 63) wcnt[wv] = y;
+    if (lane == 63) wcnt[par][wv] = y;
     __syncthreads();
     int before = 0;
-    for (int w = 0; w < wv; ++w) before += wcnt[w];
-    __syncthreads();
+    for (int w = 0; w < wv; ++w) before += wcnt[par][w];
+    par ^= 1;
     return before + (y - x);
   };
   // Top-K / top-P cut of e[] (the row's logits `lg`): tokens are ranked by
@@ -426,23 +429,32 @@ __global__ __launch_bounds__(SV_T) void k_sample_verify(StepIO io, RowLayout L) 
   // bit on an order-preserving integer key of the logit; the tokens tied at
   // the threshold are taken in id order (the thread slices are in id order).
   auto restrict_cut = [&](const float* lg) {
-    constexpr int CHMAX = (SAMPLE_VMAX + SV_T - 1) / SV_T;
+    // order-preserving keys of the slice's logits; keys past the slice are
+    // 0, below every finite logit's key and below every threshold the
+    // searches try (those are >= 1), so the searches need no range test
     uint32_t kk[CHMAX];
 #pragma unroll
     for (int j = 0; j < CHMAX; ++j) {
       const uint32_t u = v0 + j < v1 ? __float_as_uint(lg[v0 + j]) : 0u;
-      kk[j] = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+      kk[j] = v0 + j < v1 ? ((u & 0x80000000u) ? ~u : (u | 0x80000000u)) : 0u;
     }
     auto in = [&](int j) { return v0 + j < v1; };
     if (io.top_k > 0) {
       // the top_k-th largest key: the largest t with #{key >= t} >= top_k
+      // (each wave counts its keys >= c by ballots: one compare per key and
+      // a scalar popcount, no lane exchange; integer counts in any order)
       uint32_t t = 0;
       for (int b = 31; b >= 0; --b) {
         const uint32_t c = t | (1u << b);
         int n = 0;
 #pragma unroll
-        for (int j = 0; j < CHMAX; ++j) n += in(j) && kk[j] >= c;
-        if (block_count(n) >= io.top_k) t = c;
+        for (int j = 0; j < CHMAX; ++j) n += __popcll(__ballot(kk[j] >= c));
+        if (lane == 0) wcnt[par][wv] = n;
+        __syncthreads();
+        int tot = 0;
+        for (int w = 0; w < SV_T / 64; ++w) tot += wcnt[par][w];
+        par ^= 1;
+        if (tot >= io.top_k) t = c;
       }
       int ngt = 0, neq = 0;
 #pragma unroll
@@ -464,10 +476,13 @@ __global__ __launch_bounds__(SV_T) void k_sample_verify(StepIO io, RowLayout L) 
       __syncthreads();
     }
     if (io.top_p < 1.f) {
-      float loc = 0.f;
+      // this thread's weights (its own slice of e[], after the top-K cut)
+      float ev[CHMAX];
 #pragma unroll
-      for (int j = 0; j < CHMAX; ++j)
-        if (in(j)) loc += e[v0 + j];
+      for (int j = 0; j < CHMAX; ++j) ev[j] = in(j) ? e[v0 + j] : 0.f;
+      float loc = 0.f;  // (+0 for the keys past the slice: the same sum)
+#pragma unroll
+      for (int j = 0; j < CHMAX; ++j) loc += ev[j];
       const float target = io.top_p * block_fsum(loc);
       // the largest key t whose tokens at or above it hold the target
       uint32_t t = 0;
@@ -475,16 +490,15 @@ __global__ __launch_bounds__(SV_T) void k_sample_verify(StepIO io, RowLayout L) 
         const uint32_t c = t | (1u << b);
         float x = 0.f;
 #pragma unroll
-        for (int j = 0; j < CHMAX; ++j)
-          if (in(j) && kk[j] >= c) x += e[v0 + j];
+        for (int j = 0; j < CHMAX; ++j) x += kk[j] >= c ? ev[j] : 0.f;
         if (block_fsum(x) >= target) t = c;
       }
       float sgt = 0.f, seq = 0.f;
 #pragma unroll
       for (int j = 0; j < CHMAX; ++j) {
         if (!in(j)) continue;
-        if (kk[j] > t) sgt += e[v0 + j];
-        else if (kk[j] == t) seq += e[v0 + j];
+        if (kk[j] > t) sgt += ev[j];
+        else if (kk[j] == t) seq += ev[j];
       }
       const float above = block_fsum(sgt);
       float run = above + block_exscan(seq);
@@ -496,7 +510,7 @@ __global__ __launch_bounds__(SV_T) void k_sample_verify(StepIO io, RowLayout L) 
         else if (kk[j] == t) {
           if (full) e[v0 + j] = 0.f;
           else {
-            run += e[v0 + j];
+            run += ev[j];
             full = run >= target;
           }
         }
@@ -538,6 +552,48 @@ __global__ __launch_bounds__(SV_T) void k_sample_verify(StepIO io, RowLayout L) 
     const float z = red[0];
     __syncthreads();
     return z;
+  };
+  const float z = weights(row);
+  float* dst = io.sw + (size_t)b * V;
+  if ((V & 3) == 0) {
+    for (int v = 4 * tid; v < V; v += 4 * SV_T) *(float4*)&dst[v] = *(const float4*)&e[v];
+  } else {
+    for (int v = tid; v < V; v += SV_T) dst[v] = e[v];
+  }
+  if (tid == 0) io.sz[b] = z;
+}
+
+// One workgroup: the verification itself, over the weights k_sample_weights
+// left (copied into LDS for the visited row), the draws in order.
+__global__ __launch_bounds__(SV_T) void k_sample_verify(StepIO io, RowLayout L) {
+  __shared__ __align__(16) float e[SAMPLE_VMAX];
+  __shared__ float wtot[SV_T / 64];
+  __shared__ int32_t removed[VMAX_M];
+  __shared__ int32_t surv[VMAX_M];
+  __shared__ int s_nrem, s_pick, s_nsurv, s_row, s_done_pos;
+  __shared__ float s_target;
+  __shared__ int32_t emitted[LA_MAX_N];  // accepted tokens, then the drawn one
+  DevState* st = io.st;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int n1 = L.N - 1, V = io.V;
+  const int vbase = 1 + L.W * n1;
+  const int CH = (V + SV_T - 1) / SV_T;
+  const int v0 = min(V, tid * CH), v1 = min(V, v0 + CH);
+  const unsigned long long step = (unsigned long long)st->stats[ST_STEPS];
+  const int ncand = st->ncand;
+  uint32_t k = 0;  // draws used (same on every thread)
+
+  // row `row`'s weights into e[] (coalesced), return Z
+  auto weights = [&](int row) -> float {
+    const int b = row == 0 ? 0 : row - vbase + 1;
+    const float* src = io.sw + (size_t)b * V;
+    if ((V & 3) == 0) {
+      for (int v = 4 * tid; v < V; v += 4 * SV_T) *(float4*)&e[v] = *(const float4*)&src[v];
+    } else {
+      for (int v = tid; v < V; v += SV_T) e[v] = src[v];
+    }
+    __syncthreads();
+    return io.sz[b];
   };
   // residual draw: the first token v (index order, not removed) whose
   // running sum of weights reaches u * (sum of the remaining weights)
@@ -763,8 +819,16 @@ hipError_t launch_verify(const PoolDesc& pool, const StepIO& io, const RowLayout
   return hipGetLastError();
 }
 
+hipError_t launch_sample_weights(const StepIO& io, const RowLayout& lay, hipStream_t st) {
+  if (lay.M > VMAX_M || io.V > SAMPLE_VMAX || io.V < 1 || !(io.temp > 0.f) || lay.N < 2 ||
+      !io.sw || !io.sz)
+    return hipErrorInvalidValue;
+  la_launch(k_sample_weights, dim3(1 + lay.G * (lay.N - 1)), dim3(SV_T), 0, st, io, lay);
+  return hipGetLastError();
+}
+
 hipError_t launch_sample_verify(const StepIO& io, const RowLayout& lay, hipStream_t st) {
-  if (lay.M > VMAX_M || io.V > SAMPLE_VMAX || io.V < 1 || !(io.temp > 0.f))
+  if (lay.M > VMAX_M || io.V > SAMPLE_VMAX || io.V < 1 || !(io.temp > 0.f) || !io.sw || !io.sz)
     return hipErrorInvalidValue;
   la_launch(k_sample_verify, dim3(1), dim3(SV_T), 0, st, io, lay);
   return hipGetLastError();

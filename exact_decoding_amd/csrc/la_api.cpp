@@ -104,7 +104,7 @@ struct WsPlan {
 };
 
 struct Views {
-  size_t x, h, q, att, att_part, act, part, logits, amax, amax_keys, kc, vc, kb, vb, rope, pool_tok, pool_cnt,
+  size_t x, h, q, att, att_part, act, part, logits, amax, amax_keys, sw, sz, kc, vc, kb, vb, rope, pool_tok, pool_cnt,
       pool_head, pool_ctx, win, cand, ids, pos, prompt, st, total;
 };
 
@@ -178,6 +178,10 @@ Views plan_views(const Shape& s) {
   v.logits = w.take((size_t)s.M * s.V * 4);
   v.amax = w.take((size_t)s.M * 4);
   v.amax_keys = w.take((size_t)s.M * s.sp_lm.nblk * 8);
+  // sampling weights of row 0 and the verification rows (sampling sessions)
+  const size_t nsw = 1 + (size_t)s.G * (s.N - 1);
+  v.sw = w.take(nsw * s.V * 4);
+  v.sz = w.take(nsw * 4);
   const size_t kvb = (size_t)s.L * s.Hkv * s.ld_ctx * s.hd * es;
   v.kc = w.take(kvb);
   v.vc = w.take(kvb);
@@ -475,6 +479,8 @@ int enqueue_step(la_session* ss) {
   io.eos = ss->p.eos_id;
   io.gmax = s.G;
   io.logits = ss->at<float>(ss->v.logits);
+  io.sw = ss->at<float>(ss->v.sw);
+  io.sz = ss->at<float>(ss->v.sz);
   io.V = s.V;
   io.temp = ss->p.temperature;
   io.seed = (unsigned long long)ss->p.seed;
@@ -526,8 +532,10 @@ int enqueue_step(la_session* ss) {
     LA_KP(LA_PROF_ARGMAX, R * s.V * 4.0, 0,
           launch_argmax(ss->at<float>(ss->v.logits), Mc, s.V, ss->at<int32_t>(ss->v.amax), st),
           "argmax");
-  if (io.temp > 0.f)
+  if (io.temp > 0.f) {
+    LA_KP(LA_PROF_BOOK, 0, 0, launch_sample_weights(io, ss->lay, st), "sample_weights");
     LA_KP(LA_PROF_BOOK, 0, 0, launch_sample_verify(io, ss->lay, st), "sample_verify");
+  }
   LA_KP(LA_PROF_BOOK, 0, 0, launch_verify(pool, io, ss->lay, st), "verify");
   KvCommit c{};
   c.st = io.st;

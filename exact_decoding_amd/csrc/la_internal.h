@@ -258,6 +258,11 @@ struct StepIO {
   unsigned long long seed;
   int top_k;      // 0: no top-K cut (else 1 <= top_k < V)
   float top_p;    // 1: no top-P cut (else 0 < top_p < 1)
+  // the sampling weights of row 0 and of every verification row (block b:
+  // row 0 for b = 0, verification row b - 1 after), [1 + G(N-1)][V], and
+  // their sums
+  float* sw;
+  float* sz;
 };
 hipError_t launch_gather(const PoolDesc& pool, const StepIO& io, const RowLayout& lay,
                          hipStream_t st);
@@ -265,6 +270,7 @@ hipError_t launch_verify(const PoolDesc& pool, const StepIO& io, const RowLayout
                          hipStream_t st);
 // Largest vocabulary the sampling verification keeps in LDS.
 constexpr int SAMPLE_VMAX = 32768;
+hipError_t launch_sample_weights(const StepIO& io, const RowLayout& lay, hipStream_t st);
 hipError_t launch_sample_verify(const StepIO& io, const RowLayout& lay, hipStream_t st);
 hipError_t launch_philox_uniform(unsigned long long seed, unsigned long long step, int n,
                                  float* out, hipStream_t st);
