@@ -112,6 +112,7 @@ struct Shape {
   int L, d, H, Hkv, hd, F, V, dt;
   int M, rows_cap, ld_ctx;
   int N, W, G, cap, lru, by_ctx;
+  int sampling;  // temperature > 0: the sampling weights buffers exist
   SplitPlan sp_qkv, sp_o, sp_gu, sp_d, sp_lm;
   double pc_qkv, pc_o, pc_gu, pc_d;  // mean pieces per column block (profile bytes)
   int att_mfma, att_nsplit;  // MFMA-attention prefix chunks (0 = per-row kernel only)
@@ -129,6 +130,7 @@ Shape make_shape(const la_model* m, const la_decode_params* p) {
   s.cap = p->pool_cap > 0 ? p->pool_cap : (s.G > 0 ? s.G : 1);
   s.lru = (p->flags & LA_POOL_LRU) != 0;
   s.by_ctx = (p->flags & LA_POOL_CONTEXT) != 0;
+  s.sampling = p->temperature > 0.f;
   s.M = 1 + (s.W + s.G) * (s.N - 1);
   s.ld_ctx = p->max_ctx;
   s.rows_cap = s.M > p->max_ctx ? s.M : p->max_ctx;
@@ -179,7 +181,7 @@ Views plan_views(const Shape& s) {
   v.amax = w.take((size_t)s.M * 4);
   v.amax_keys = w.take((size_t)s.M * s.sp_lm.nblk * 8);
   // sampling weights of row 0 and the verification rows (sampling sessions)
-  const size_t nsw = 1 + (size_t)s.G * (s.N - 1);
+  const size_t nsw = s.sampling ? 1 + (size_t)s.G * (s.N - 1) : 0;
   v.sw = w.take(nsw * s.V * 4);
   v.sz = w.take(nsw * 4);
   const size_t kvb = (size_t)s.L * s.Hkv * s.ld_ctx * s.hd * es;

@@ -70,9 +70,14 @@ def test_session_bytes_and_param_validation():
     assert n > 0
     p_ar = B.DecodeParams(5, 15, 15, 0, 400, 256, -1, B.LA_AR)
     assert 0 < B.la_session_bytes(m, p_ar) < n
-    # a temperature and a seed change nothing in the workspace
+    # a temperature adds the sampling weights of row 0 and the 60
+    # verification rows (vocab floats each, plus their sums; 256-byte aligned)
     p_s = B.DecodeParams(5, 15, 15, 0, 400, 256, -1, B.LA_PROMPT_REF, 0.8, 0, 12345)
-    assert B.la_session_bytes(m, p_s) == n
+    ns = B.la_session_bytes(m, p_s)
+    align = lambda b: (b + 255) // 256 * 256
+    assert ns == n + align(61 * 4000 * 4) + align(61 * 4)
+    # the seed changes nothing
+    assert B.la_session_bytes(m, B.DecodeParams(5, 15, 15, 0, 400, 256, -1, B.LA_PROMPT_REF, 0.8, 0, 7)) == ns
     # nor does the pool's eviction policy
     p_l = B.DecodeParams(5, 15, 15, 0, 400, 256, -1,
                          B.LA_PROMPT_REF | B.LA_POOL_LRU | B.LA_POOL_CONTEXT)
@@ -80,7 +85,7 @@ def test_session_bytes_and_param_validation():
     # nor do top-K / top-P (K past the vocabulary and p = 1 are no cut)
     for k, pp in [(40, 0.9), (1, 0.0), (10 ** 6, 1.0)]:
         p_k = B.DecodeParams(5, 15, 15, 0, 400, 256, -1, B.LA_PROMPT_REF, 0.8, k, 12345, pp)
-        assert B.la_session_bytes(m, p_k) == n
+        assert B.la_session_bytes(m, p_k) == ns
     for bad in [B.DecodeParams(1, 4, 4, 0, 100, 10, -1, 0), B.DecodeParams(17, 4, 4, 0, 100, 10, -1, 0),
                 B.DecodeParams(3, -1, 4, 0, 100, 10, -1, 0), B.DecodeParams(3, 4, 4, 0, 100, 0, -1, 0),
                 B.DecodeParams(3, 4, 4, 0, 100, 10, 4000, 0), B.DecodeParams(3, 4, 4, 0, 100, 10, -1, 128),
