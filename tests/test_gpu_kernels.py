@@ -141,6 +141,8 @@ def _run_attn(dev, P, ld_ctx, H, Hkv, hd, N, W, G, dtype, tdt, M):
     (512, 32, 32, 128, 5, 15, 15, B.LA_BF16),
     (513, 32, 32, 128, 7, 7, 7, B.LA_BF16),
     (2048, 32, 32, 128, 5, 15, 15, B.LA_BF16),
+    (1500, 8, 2, 128, 3, 4, 4, B.LA_BF16),
+    (1100, 16, 2, 128, 5, 7, 7, B.LA_BF16),
 ])
 def test_attention_matches_oracle(P, H, Hkv, hd, N, W, G, dtype):
     print(f"attention P={P} H={H} Hkv={Hkv} hd={hd} N={N} W={W} G={G}", flush=True)
@@ -154,10 +156,13 @@ def test_attention_matches_oracle(P, H, Hkv, hd, N, W, G, dtype):
     assert np.abs(got - ref).max() < tol
 
 
-@pytest.mark.parametrize("P,W,G", [(5, 3, 3), (63, 3, 3), (64, 3, 3), (130, 3, 3), (300, 3, 3),
-                                   (525, 3, 3), (1100, 3, 3), (130, 15, 15), (300, 15, 15),
-                                   (525, 15, 15), (1100, 15, 15), (300, 20, 20), (1100, 20, 20)])
-def test_attention_verification_row_equals_ar_query(P, W, G):
+@pytest.mark.parametrize("P,W,G,H,Hkv", [
+    (5, 3, 3, 4, 4), (63, 3, 3, 4, 4), (64, 3, 3, 4, 4), (130, 3, 3, 4, 4), (300, 3, 3, 4, 4),
+    (525, 3, 3, 4, 4), (1100, 3, 3, 4, 4), (130, 15, 15, 4, 4), (300, 15, 15, 4, 4),
+    (525, 15, 15, 4, 4), (1100, 15, 15, 4, 4), (300, 20, 20, 4, 4), (1100, 20, 20, 4, 4),
+    # grouped-query heads
+    (300, 3, 3, 8, 2), (1100, 3, 3, 8, 2), (1100, 7, 7, 16, 2), (1100, 15, 15, 8, 2)])
+def test_attention_verification_row_equals_ar_query(P, W, G, H, Hkv):
     """Verification row (g, i) == one query at P+i over a cache holding the
     prefix and the row's chain (what an autoregressive step computes).
     Below 1024 committed positions each wave of the MFMA prefix part holds
@@ -165,8 +170,8 @@ def test_attention_verification_row_equals_ar_query(P, W, G):
     on a workgroup takes 128 rows and every wave runs two groups together on
     each tile (W = G = 15: 121 rows; W = G = 20: 161 rows, a 128-row block
     and a 33-row one), so the rows go through the two-group path and the
-    query through the one-group path."""
-    H, Hkv, hd, N = 4, 4, 128, 5
+    query through the one-group path; also with grouped-query heads."""
+    hd, N = 128, 5
     M, ld, dev, host, tdt = _rand_attn(P, H, Hkv, hd, N, W, G, B.LA_BF16, seed=P, ld_ctx=P + 16)
     out = _run_attn(dev, P, ld, H, Hkv, hd, N, W, G, B.LA_BF16, tdt, M)
     q, kc, vc, kb, vb = dev
