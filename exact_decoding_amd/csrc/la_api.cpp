@@ -104,8 +104,8 @@ struct WsPlan {
 };
 
 struct Views {
-  size_t x, h, q, att, att_part, act, part, logits, amax, amax_keys, sw, sz, kc, vc, kb, vb, rope, pool_tok, pool_cnt,
-      pool_head, pool_ctx, win, cand, ids, pos, prompt, st, total;
+  size_t x, h, q, att, att_part, act, part, logits, amax, amax_keys, sw, sz, kc, vc, kb, vb, rope,
+      pool_tok, pool_cnt, pool_head, pool_ctx, win, cand, ids, pos, prompt, st, total;
 };
 
 struct Shape {
