@@ -44,6 +44,10 @@ def parse():
     ap.add_argument("--W", type=int, default=15)
     ap.add_argument("--G", type=int, default=15)
     ap.add_argument("--prompt-len", type=int, default=128)
+    ap.add_argument("--prompt", choices=["auto", "zipf", "code"], default="auto",
+                    help="prompt recipe: Zipf(1.1) ids with repeated spans, or code-like lines "
+                         "(20 lines of 24 ids from a 2000-id sub-vocabulary, 40%% repeated); "
+                         "auto: code for the 13B shape, Zipf otherwise")
     ap.add_argument("--max-new", type=int, default=256)
     ap.add_argument("--profile-steps", type=int, default=32)
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
@@ -603,7 +607,13 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] weights ready in {time.time() - t0:.1f}s")
     model = Model(shape, dev)
-    prompt = synth.prompt_zipf_spans(shape.vocab, length=args.prompt_len, seed=1)
+    recipe = args.prompt if args.prompt != "auto" else ("code" if shape.name == "codellama13b" else "zipf")
+
+    def make_prompt(seed):
+        if recipe == "code":
+            return synth.prompt_code_lines(shape.vocab, length=args.prompt_len, seed=seed)
+        return synth.prompt_zipf_spans(shape.vocab, length=args.prompt_len, seed=seed)
+    prompt = make_prompt(1)
     window = synth.gen_window(N, W, shape.vocab, seed=2)
     graph = not args.no_graph
     if args.sweep:
@@ -707,7 +717,7 @@ def main():
     # step compression over prompt seeds 0.. (one whole generation each)
     S_seeds = []
     for ps in range(args.seed_sweep):
-        pr = synth.prompt_zipf_spans(shape.vocab, length=args.prompt_len, seed=ps)
+        pr = make_prompt(ps)
         ses = model.session(pr, N, W, G, args.max_new, window=window, prompt_ref=True,
                             graph=graph, temperature=args.temperature, seed=args.seed,
                             top_k=args.top_k, top_p=args.top_p)
@@ -771,9 +781,10 @@ def main():
         "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if shape.dtype == "bf16" else "f32", "data": "synthetic",
         "config": {"workload": f"lookahead decoding step, {shape.name} shape random-init, batch 1, "
-                               f"prompt {len(prompt)} Zipf(1.1)+3 repeated spans, prompt as reference, "
+                               f"prompt {len(prompt)} " + ("code-like lines (40% repeated)" if recipe == "code" else "Zipf(1.1)+3 repeated spans") + ", prompt as reference, "
                                f"{args.max_new} new tokens per generation",
-                   "N": N, "W": W, "G": G, "rows_per_step": M, "parallelism": "single GPU",
+                   "prompt": recipe, "N": N, "W": W, "G": G, "rows_per_step": M,
+                   "parallelism": "single GPU",
                    "graph": graph, "temperature": args.temperature, "top_k": args.top_k,
                    "top_p": args.top_p, "pool": "lru" if args.pool_lru else "fifo",
                    "pool_cap": args.pool_cap or G},
