@@ -59,8 +59,11 @@ __device__ __forceinline__ void lds_barrier() {
 // Weights come in the packed layout (see la.h): MFMA step j of chunk c of a
 // 16-row stripe is one contiguous KB holding, for lane (q = lane/16,
 // r = lane%16), k in [64c + 32j + 8q, +8) of row r; the x tile is read with
-// the same k order.  A wave therefore streams each of its two stripes
-// sequentially.  LDS x rows are 128 bytes with the 16-byte pieces
+// the same k order.  The stripes of one 128-row column block sit side by
+// side for each chunk, and the chunks of a block, then the blocks, follow
+// each other: the (column block, K chunk) units lie in memory in the order
+// the split plan deals them out, so every workgroup streams one contiguous
+// range whatever the plan.  LDS x rows are 128 bytes with the 16-byte pieces
 // XOR-swizzled by (row/2) mod 8 so the A-fragment reads hit distinct banks.
 constexpr int XR = 3;  // LDS stages of the x tile
 
@@ -190,27 +193,30 @@ __global__ __launch_bounds__(320) void k_gemm_bf16(GemmDesc g) {
   // the segment reads stripe 0 (its output is discarded at the store):
   // unpredicated loads let the compiler count outstanding loads exactly
   // instead of draining them at branch joins.
-  auto setup = [&](int b, const bf16_t* (&wrow)[2], int& sbase, int& segn, int& nl)
+  auto setup = [&](int b, const bf16_t* (&wrow)[2], int& sbase, int& segn, int& nl, int& cs)
       __attribute__((always_inline)) {
     int si;
     placement(b, wave, sbase, segn, nl, si);
     const bf16_t* W = (const bf16_t*)g.seg[si].w;
+    const int bl = (nl - wave * 32) >> 7;                 // block within the segment
+    const int ns = min(8, (segn + 15) / 16 - 8 * bl);      // its stripes
+    cs = ns * 1024;                                        // one chunk of the block
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const int stripe = (nl + t * 16) >> 4;
+      const int sb = 2 * wave + t;
       const int ok = nl + t * 16 < segn;
-      wrow[t] = W + (size_t)(ok ? stripe : 0) * nch * 1024 + lane * 8;
+      wrow[t] = W + ((size_t)bl * nch * 8 + (ok ? sb : 0)) * 1024 + lane * 8;
     }
   };
   const bf16_t* wA[2];
   const bf16_t* wB[2];
-  int sbA, segnA, nlA, sbB = 0, segnB = 0, nlB = 0;
-  setup(bA, wA, sbA, segnA, nlA);
-  if (n > nA) setup(bA + 1, wB, sbB, segnB, nlB);
-  else { wB[0] = wA[0]; wB[1] = wA[1]; }
+  int sbA, segnA, nlA, csA, sbB = 0, segnB = 0, nlB = 0, csB = 0;
+  setup(bA, wA, sbA, segnA, nlA, csA);
+  if (n > nA) setup(bA + 1, wB, sbB, segnB, nlB, csB);
+  else { wB[0] = wA[0]; wB[1] = wA[1]; csB = csA; }
   // weight rows of run chunk t, offset by the chunk's K position
   auto wptr = [&](int t, int tt) __attribute__((always_inline)) {
-    return t < nA ? wA[tt] + (size_t)(cA + t) * 1024 : wB[tt] + (size_t)(t - nA) * 1024;
+    return t < nA ? wA[tt] + (size_t)(cA + t) * csA : wB[tt] + (size_t)(t - nA) * csB;
   };
 
   f32x4_t acc[MT][2];
@@ -413,29 +419,32 @@ void k_gemm4(GemmDesc g) {
     segn = g.seg[si].n;
     nl = col0 - sbase + wave * 32;
   };
-  auto setup = [&](int b, const bf16_t* (&wrow)[2], int& sbase, int& segn, int& nl)
+  auto setup = [&](int b, const bf16_t* (&wrow)[2], int& sbase, int& segn, int& nl, int& cs)
       __attribute__((always_inline)) {
     int si;
     placement(b, sbase, segn, nl, si);
     const bf16_t* W = (const bf16_t*)g.seg[si].w;
+    const int bl = (nl - wave * 32) >> 7;                 // block within the segment
+    const int ns = min(8, (segn + 15) / 16 - 8 * bl);      // its stripes
+    cs = ns * 1024;                                        // one chunk of the block
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const int stripe = (nl + t * 16) >> 4;
+      const int sb = 2 * wave + t;
       const int ok = nl + t * 16 < segn;
-      wrow[t] = W + (size_t)(ok ? stripe : 0) * nch * 1024 + lane * 8;
+      wrow[t] = W + ((size_t)bl * nch * 8 + (ok ? sb : 0)) * 1024 + lane * 8;
     }
   };
   const bf16_t* wA[2];
   const bf16_t* wB[2];
-  int sbA, segnA, nlA, sbB = 0, segnB = 0, nlB = 0;
-  setup(bA, wA, sbA, segnA, nlA);
-  if (n > nA) setup(bA + 1, wB, sbB, segnB, nlB);
-  else { wB[0] = wA[0]; wB[1] = wA[1]; }
+  int sbA, segnA, nlA, csA, sbB = 0, segnB = 0, nlB = 0, csB = 0;
+  setup(bA, wA, sbA, segnA, nlA, csA);
+  if (n > nA) setup(bA + 1, wB, sbB, segnB, nlB, csB);
+  else { wB[0] = wA[0]; wB[1] = wA[1]; csB = csA; }
   auto load_w = [&](int t, u32x4_t (&dst)[2][2]) __attribute__((always_inline)) {
     const int tc = t < n ? t : n - 1;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      const bf16_t* p = tc < nA ? wA[tt] + (size_t)(cA + tc) * 1024 : wB[tt] + (size_t)(tc - nA) * 1024;
+      const bf16_t* p = tc < nA ? wA[tt] + (size_t)(cA + tc) * csA : wB[tt] + (size_t)(tc - nA) * csB;
       dst[tt][0] = *(const u32x4_t*)p;
       dst[tt][1] = *(const u32x4_t*)(p + 512);
     }
@@ -609,7 +618,9 @@ __global__ __launch_bounds__(128) void k_pack_bf16(const bf16_t* __restrict__ sr
   const int k = 64 * c + 32 * j + 8 * (lane >> 4);
   u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
   if (row < N) v = *(const u32x4_t*)(src + (size_t)row * K + k);
-  *(u32x4_t*)(dst + (((size_t)s * nch + c) * 2 + j) * 512 + lane * 8) = v;
+  const int b = s >> 3, sb = s & 7;
+  const int ns = min(8, (N + 15) / 16 - 8 * b);  // stripes of column block b
+  *(u32x4_t*)(dst + ((size_t)b * nch * 8 + (size_t)c * ns + sb) * 1024 + j * 512 + lane * 8) = v;
 }
 
 }  // namespace

@@ -157,12 +157,17 @@ typedef struct la_session la_session;
 
 /* Packed bf16 weight layout (what la_model_load and la_kernel_gemm take for
  * the projection and LM-head matrices of bf16 models).  A row-major
- * W[N][K] (K a multiple of 64) is stored as ceil(N/16) stripes of 16 rows;
- * stripe s holds K/64 blocks of 2048 bytes, block c holding
+ * W[N][K] (K a multiple of 64) is cut into S = ceil(N/16) stripes of 16 rows
+ * and into column blocks of 8 stripes (128 rows; the last block holds the
+ * ns(b) = min(8, S - 8b) stripes left).  For block b, K chunk c (of 64) and
+ * stripe t < ns(b) of the block (stripe s = 8b + t), 2048 bytes hold
  *   element (j, lane, e) = W[16s + lane%16][64c + 32j + 8(lane/16) + e]
- * at byte offset ((s*(K/64) + c)*2 + j)*1024 + lane*16 + e*2, for j in {0,1},
- * lane in [0,64), e in [0,8); rows >= N are zero.  Every 1 KB is one MFMA
- * B operand of 64 lanes, so a GEMM streams each stripe sequentially. */
+ * at byte offset (b*(K/64)*8 + c*ns(b) + t)*2048 + j*1024 + lane*16 + e*2,
+ * for j in {0,1}, lane in [0,64), e in [0,8); rows >= N are zero.  Every
+ * 1 KB is one MFMA B operand of 64 lanes.  A (block, chunk) unit is one
+ * contiguous run, and units follow in block-major order, the order in which
+ * the GEMM deals them to its workgroups, so each workgroup reads one
+ * contiguous range.  Total ceil(N/16)*16*K*2 bytes. */
 size_t la_packed_bytes(int32_t N, int32_t K);
 /* Pack a row-major bf16 W[N][K] (device) into `dst` (device, la_packed_bytes
  * bytes).  Enqueued on `hip_stream`. */

@@ -44,22 +44,27 @@ def _gemm(x, w, dtype=B.LA_BF16, wp=None):
     return y
 
 
-def test_pack_layout():
-    """The packed layout places W[16s + lane%16][64c + 32j + 8(lane/16) + e]
-    at element ((s*(K/64) + c)*2 + j)*512 + lane*8 + e; rows past N are 0."""
-    N, K = 37, 128
+@pytest.mark.parametrize("N,K", [(37, 128), (300, 192)])
+def test_pack_layout(N, K):
+    """The packed layout places W[16s + lane%16][64c + 32j + 8(lane/16) + e],
+    s = 8b + t, at element ((b*(K/64)*8 + c*ns(b) + t)*2 + j)*512 + lane*8 + e
+    with ns(b) = min(8, ceil(N/16) - 8b) stripes in column block b; rows past
+    N are 0.  N = 300: two full column blocks and a last one of 3 stripes."""
     w = torch.arange(N * K, dtype=torch.float32).reshape(N, K).to(torch.bfloat16).to(DEV)
     got = _pack(w).view(torch.bfloat16).float().cpu().numpy()
     wf = w.float().cpu().numpy()
     nch = K // 64
-    ref = np.zeros(((N + 15) // 16) * 16 * K, dtype=np.float32)
-    for s_ in range((N + 15) // 16):
+    S = (N + 15) // 16
+    ref = np.zeros(S * 16 * K, dtype=np.float32)
+    for s_ in range(S):
+        b, t = divmod(s_, 8)
+        ns = min(8, S - 8 * b)
         for c in range(nch):
             for j in range(2):
                 for lane in range(64):
                     row = 16 * s_ + lane % 16
                     k = 64 * c + 32 * j + 8 * (lane // 16)
-                    base = ((s_ * nch + c) * 2 + j) * 512 + lane * 8
+                    base = ((b * nch * 8 + c * ns + t) * 2 + j) * 512 + lane * 8
                     if row < N:
                         ref[base:base + 8] = wf[row, k:k + 8]
     np.testing.assert_array_equal(got, ref)
