@@ -232,7 +232,7 @@ __global__ __launch_bounds__(320) void k_gemm_bf16(GemmDesc g) {
     for (int tt = 0; tt < 2; ++tt) {
       const bf16_t* p = wptr(t, tt);
       // streaming hint: each weight line is used once; measured 7-10% faster
-      // at one row tile (it did not help the multi-tile kernel)
+      // at one row tile
       dst[tt][0] = __builtin_nontemporal_load((const u32x4_t*)p);
       dst[tt][1] = __builtin_nontemporal_load((const u32x4_t*)(p + 512));
     }
@@ -445,8 +445,11 @@ void k_gemm4(GemmDesc g) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const bf16_t* p = tc < nA ? wA[tt] + (size_t)(cA + tc) * csA : wB[tt] + (size_t)(tc - nA) * csB;
-      dst[tt][0] = *(const u32x4_t*)p;
-      dst[tt][1] = *(const u32x4_t*)(p + 512);
+      // streaming hint: each weight line is used once, and the lines then
+      // leave the L2 room for the x tile and for the small tensors the
+      // attention and epilogue kernels read
+      dst[tt][0] = __builtin_nontemporal_load((const u32x4_t*)p);
+      dst[tt][1] = __builtin_nontemporal_load((const u32x4_t*)(p + 512));
     }
   };
 
