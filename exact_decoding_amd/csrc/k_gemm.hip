@@ -547,7 +547,8 @@ void k_gemm4(GemmDesc g) {
   }
 
   // this wave's parked rows -> piece `slot`: lane l writes columns 4(l%8)..+4
-  // of rows l/8, l/8 + 8, ...
+  // of rows l/8, l/8 + 8, ...  The 16-byte stores carry the streaming hint:
+  // the pieces are read once, by the next kernel, on other XCDs
   const bool vec_ok = (g.N & 3) == 0;
   auto store_rows = [&](int slot, int sbase, int segn, int nl) __attribute__((always_inline)) {
     if (!g.part) return;
@@ -560,7 +561,7 @@ void k_gemm4(GemmDesc g) {
       const f32x4_t v = *(const f32x4_t*)(pk + rr * PKS + c4);
       float* dst = out + (size_t)(row0 + rr) * g.N + sbase + nloc;
       if (vec_ok && nloc + 3 < segn) {
-        *(f32x4_t*)dst = v;
+        __builtin_nontemporal_store(v, (f32x4_t*)dst);
       } else {
 #pragma unroll
         for (int k = 0; k < 4; ++k)
