@@ -32,16 +32,18 @@ __device__ __forceinline__ float sum_pieces(const float* __restrict__ part, cons
 }
 
 // The same sum for four consecutive columns (col a multiple of 4, N too; the
-// four share a column block), with 16-byte loads.
+// four share a column block), with 16-byte loads.  The pieces are read once:
+// the loads carry the streaming hint, so they do not push the x tiles, KV
+// rows and other reused data out of the L2.
 template <int NP>
 __device__ __forceinline__ f32x4_t sum_pieces4(const float* __restrict__ part, const SplitPlan& sp,
                                                int rows_pad, int N, int m, int col) {
-  if (NP == 1) return *(const f32x4_t*)(part + (size_t)m * N + col);
+  if (NP == 1) return __builtin_nontemporal_load((const f32x4_t*)(part + (size_t)m * N + col));
   const int np = plan_pieces(sp, col / NWG);
   f32x4_t p[NP];
 #pragma unroll
   for (int s = 0; s < NP; ++s)
-    p[s] = s < np ? *(const f32x4_t*)(part + ((size_t)s * rows_pad + m) * N + col)
+    p[s] = s < np ? __builtin_nontemporal_load((const f32x4_t*)(part + ((size_t)s * rows_pad + m) * N + col))
                   : f32x4_t{0.f, 0.f, 0.f, 0.f};
   f32x4_t v = p[0];
 #pragma unroll
