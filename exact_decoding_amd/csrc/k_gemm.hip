@@ -598,18 +598,24 @@ void k_gemm4(GemmDesc g) {
   }
 }
 
-// fp32 models: one thread per output element, K summed in order.
-__global__ __launch_bounds__(64) void k_gemm_f32(GemmDesc g) {
-  const int n = blockIdx.x * 64 + threadIdx.x;
+// fp32 models: one wave per output element.  Lane l sums k = l, l + 64, ...
+// in order, then the 64 lane sums are added by a fixed xor-shuffle tree, so
+// an element's sum does not depend on the row count; the lanes read the
+// weight row and the x row contiguously.
+__global__ __launch_bounds__(256) void k_gemm_f32(GemmDesc g) {
+  const int lane = threadIdx.x & 63;
+  const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int m = blockIdx.y;
-  if (n >= g.N || m >= g.rows) return;
+  if (n >= g.N || m >= g.rows) return;  // whole waves
   int si = 0, sbase = 0;
   while (si < g.nseg - 1 && n >= sbase + g.seg[si].n) { sbase += g.seg[si].n; ++si; }
   const float* w = (const float*)g.seg[si].w + (size_t)(n - sbase) * g.K;
   const float* x = (const float*)g.x + (size_t)m * g.K;
   float acc = 0.f;
-  for (int k = 0; k < g.K; ++k) acc = fmaf(x[k], w[k], acc);
-  g.part[(size_t)m * g.N + n] = acc;
+  for (int k = lane; k < g.K; k += 64) acc = fmaf(x[k], w[k], acc);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+  if (lane == 0) g.part[(size_t)m * g.N + n] = acc;
 }
 
 // dst block (stripe s, chunk c): element (j, lane, e) = W[16s + lane%16][64c + 32j + 8(lane/16) + e]
@@ -676,8 +682,8 @@ SplitPlan gemm_plan(int N, int K, int dtype) {
 
 hipError_t launch_gemm(const GemmDesc& g, int dtype, hipStream_t st) {
   if (dtype == LA_F32) {
-    dim3 grid((g.N + 63) / 64, g.rows);
-    la_launch(k_gemm_f32, grid, dim3(64), 0, st, g);
+    dim3 grid((g.N + 3) / 4, g.rows);
+    la_launch(k_gemm_f32, grid, dim3(256), 0, st, g);
     return hipGetLastError();
   }
   if (g.sp.nblk != (g.N + NWG - 1) / NWG || g.sp.nch != g.K / KC) return hipErrorInvalidValue;
