@@ -107,21 +107,26 @@ __device__ __forceinline__ int row_pos(const AttnDesc& a, int r, int Pc) {
 // kernel's (m, l, o) partials of [0, F) in chunk order.
 constexpr int TT = 32;  // per-row tile (positions)
 
-// half of dot(q, k): dimensions [h0, h0 + HD/2), four interleaved partial
-// sums (dimension d to partial d mod 4, each in increasing d) added as
-// (p0+p1)+(p2+p3)
+// half of dot(q, k): dimensions [h0, h0 + HD/2) in four interleaved partial
+// sums, each in increasing order, added as (p0+p1)+(p2+p3).  bf16: q is
+// kept as bf16 pairs (word w = dimensions 2w, 2w+1 of the half) and pair p
+// goes to partial p mod 4 through the packed dot (v_dot2c_f32_bf16: both
+// products and the partial added in one instruction); fp32: dimension d
+// to partial d mod 4.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 template <int HD>
 __device__ __forceinline__ float dot_half(const float* qs, const u32x4_t (&k)[HD / 16], bf16_t) {
+  const u32x4_t* qw = (const u32x4_t*)qs;
   float a[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int c = 0; c < HD / 16; ++c) {
+    const u32x4_t qv = qw[c];
+    const uint32_t qe[4] = {qv.x, qv.y, qv.z, qv.w};
     const uint32_t w[4] = {k[c].x, k[c].y, k[c].z, k[c].w};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      a[(2 * e) & 3] = fmaf(qs[8 * c + 2 * e], __uint_as_float(w[e] << 16), a[(2 * e) & 3]);
-      a[(2 * e + 1) & 3] =
-          fmaf(qs[8 * c + 2 * e + 1], __uint_as_float(w[e] & 0xFFFF0000u), a[(2 * e + 1) & 3]);
-    }
+    for (int e = 0; e < 4; ++e)
+      a[e] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qe[e]),
+                                             __builtin_bit_cast(bf16x2_t, w[e]), a[e], false);
   }
   return (a[0] + a[1]) + (a[2] + a[3]);
 }
@@ -256,7 +261,11 @@ __device__ __forceinline__ void tail_row(const AttnDesc& a, int h, int r, TailLd
   PartRing<HD> R;
 #pragma unroll
   for (int i = 0; i < PartRing<HD>::NPRE; ++i) ring_load<HD>(a, h, r, nch, i, i, R, d0, down);
-  for (int i = lane; i < HD; i += 64) qs[i] = ld_f(q + i);
+  if (sizeof(T) == 2) {  // bf16 pairs, one word per two dimensions
+    for (int i = lane; i < HD / 2; i += 64) ((uint32_t*)qs)[i] = ((const uint32_t*)q)[i];
+  } else {
+    for (int i = lane; i < HD; i += 64) qs[i] = ld_f(q + i);
+  }
 
   // tiles of TT positions over [F, pos]
   for (int base = F; base <= pos; base += TT) {
@@ -278,7 +287,8 @@ __device__ __forceinline__ void tail_row(const AttnDesc& a, int h, int r, TailLd
         *(u32x4_t*)((char*)(vs + slot * VSTRIDE + half * (HD / 2)) + 16 * e) = vr[e];
     }
     wave_lds_sync();
-    const float mine = on ? dot_half<HD>(qs + half * (HD / 2), kr, T()) : 0.f;
+    const float mine =
+        on ? dot_half<HD>(qs + half * (sizeof(T) == 2 ? HD / 4 : HD / 2), kr, T()) : 0.f;
     const float other = __shfl_xor(mine, 1, 64);
     const float sc = on ? ((half ? other : mine) + (half ? mine : other)) * scale : -INFINITY;
     const float mp = wave_max(sc);
