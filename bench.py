@@ -745,8 +745,9 @@ def main():
                     agg[k][f] += v[f]
     ses.close()
     P_avg = P_sum / max(n_prof, 1)
-    # the dominant kernel is the projection GEMM (k_gemm4 at M = 121); its
-    # launches are the four projections per layer plus the LM head
+    # the dominant kernel is the projection GEMM at M = 121 (k_gemm4, or
+    # k_gemm_dma for the short-run shapes); its launches are the four
+    # projections per layer plus the LM head
     g = {f: agg["gemm"][f] + agg["lm_head"][f] for f in agg["gemm"]}
     gemm_ms = g["ms"] / g["launches"]
     gemm_bytes = g["bytes"] / g["launches"]
@@ -799,7 +800,7 @@ def main():
         "step_hbm": {"bytes_per_step": step_bytes, "GBps": step_gbps, "frac": step_gbps / HBM_PEAK_GBPS,
                      "frac_of_achievable": step_gbps / read_gbps if read_gbps else None,
                      "P_avg": P_avg},
-        "roofline": {"kernel": "projection GEMM k_gemm4 at M = 121 (QKV, O, gate/up, down and LM head)",
+        "roofline": {"kernel": "projection GEMM (k_gemm4 / k_gemm_dma) at M = 121 (QKV, O, gate/up, down and LM head)",
                      "bound": "hbm",
                      "achieved": gemm_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": gemm_gbps / HBM_PEAK_GBPS, "traffic": gemm_traffic(),

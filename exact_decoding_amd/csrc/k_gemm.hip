@@ -12,6 +12,8 @@
 // decodes relies on.
 #include "la_internal.h"
 
+#include <type_traits>
+
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
@@ -598,6 +600,238 @@ void k_gemm4(GemmDesc g) {
   }
 }
 
+// Loader / consumer form of the multi-row kernel, for 8 row tiles and
+// short runs (no argmax keys).  Eight waves:
+//  * waves 4-5 copy each chunk's weights (one contiguous 16 KB unit of the
+//    packed layout) into a ring of SW LDS stages, SW-1 chunks ahead;
+//  * waves 6-7 copy the chunk's x tile into a ring of SX stages;
+//  * waves 0-3 only read the rings and run the MFMAs, in the same order as
+//    k_gemm4 and k_gemm_bf16 (so the sums are the same bits).
+// The copies go global -> LDS directly (LDS DMA, 16 bytes a lane, lane l's
+// bytes at the stage base + 16 l), so a loader's issue is never held up by
+// MFMA or LDS work.  One barrier per chunk for all eight waves: a loader
+// waits for its copies of chunk t (its load counter runs in order) before
+// barrier t, and after it refills the stages the consumers left at it.
+// Both pieces (blocks bA and bA + 1) stay in registers until the stream
+// ends: stores between the weight loads slow the stream down.
+// Measured against k_gemm4 inside the 7B and 13B steps, this form ends a
+// run of up to ~22 chunks sooner (its loaders are SW-1 chunks ahead from
+// the first instruction) but streams the long runs more slowly.
+typedef __attribute__((address_space(3))) void lds_void;
+// s_waitcnt immediate for vmcnt(v) alone (gfx9 bit layout)
+__device__ constexpr int vmcnt_imm(int v) { return (v & 15) | ((v >> 4) << 14) | 0x70 | 0xF00; }
+template <int MT>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_gemm_dma(GemmDesc g) {
+  constexpr int SW = 7, SX = 3;  // weight and x stages
+  constexpr int WST = 8 * 1024;           // bf16 of one weight unit (8 stripes x 2 KB)
+  constexpr int XST = MT * 16 * 64;       // bf16 of one x tile
+  static_assert(MT == 8, "two x loader waves copy 8 KB each");
+  static_assert((SW * WST + SX * XST) * 2 <= 160 * 1024, "LDS");
+  static_assert(SW * WST * 2 >= 4 * MT * 16 * 36 * 4, "the park reuses the weight ring");
+  __shared__ __align__(16) bf16_t wring[SW * WST];
+  __shared__ __align__(16) bf16_t xring[SX * XST];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wg = blockIdx.x, mb = blockIdx.z;
+  const int K = g.K;
+  const int nch = g.sp.nch;
+  const int U = g.sp.nblk * nch;
+  const int u0 = (int)((long long)wg * U / g.sp.G);
+  const int u1 = (int)((long long)(wg + 1) * U / g.sp.G);
+  const int n = u1 - u0;
+  const int bA = u0 / nch, cA = u0 - bA * nch;
+  const int nA = min(n, nch - cA);
+  const int row0 = mb * 128;
+  const int xrows = g.rows - row0;
+  auto placement = [&](int b, int& sbase, int& segn, int& si) __attribute__((always_inline)) {
+    const int col0 = b * NWG;
+    si = 0;
+    sbase = 0;
+    while (si < g.nseg - 1 && col0 >= sbase + g.seg[si].n) { sbase += g.seg[si].n; ++si; }
+    segn = g.seg[si].n;
+  };
+  // loader loop (each loader wave issues 8 copies a chunk): wait for chunk
+  // t (younger chunks t+1 .. t+S-2 may fly), barrier t, then chunk t+S-1
+  // into the stage chunk t-1 left
+  auto loader = [&](auto issue, auto s_tag) __attribute__((always_inline)) {
+    constexpr int S = decltype(s_tag)::value;
+    for (int t = 0; t < S - 1 && t < n; ++t) issue(t);
+    for (int t = 0; t < n; ++t) {
+      if (t + S - 2 <= n - 1)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 2) * 8));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      lds_barrier();
+      if (t + S - 1 < n) issue(t + S - 1);
+    }
+    lds_barrier();  // barrier n: the consumers' park reuses the weight ring
+  };
+
+  if (wave == 4 || wave == 5) {
+    // weights: wave 4 + lw copies stripes 4 lw .. 4 lw + 3 (both MFMA steps)
+    const int lw = wave - 4;
+    const bf16_t* ubase[2];
+    int uns[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int b = bA + k;
+      int sbase = 0, segn = 0, si = 0;
+      placement(b < g.sp.nblk ? b : bA, sbase, segn, si);
+      const int bl = ((b < g.sp.nblk ? b : bA) * NWG - sbase) >> 7;
+      uns[k] = min(8, (segn + 15) / 16 - 8 * bl);
+      ubase[k] = (const bf16_t*)g.seg[si].w + (size_t)bl * nch * 8 * 1024;
+    }
+    auto issue = [&](int t) __attribute__((always_inline)) {
+      const int k = t < nA ? 0 : 1;
+      const int c = t < nA ? cA + t : t - nA;
+      const int ns = uns[k];
+      const bf16_t* unit = ubase[k] + (size_t)c * ns * 1024;
+      bf16_t* st = wring + (t % SW) * WST;
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const int sb = 4 * lw + tt;
+        const int src = sb < ns ? sb : 0;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          __builtin_amdgcn_global_load_lds((const void*)(unit + src * 1024 + j * 512 + lane * 8),
+                                           (lds_void*)(st + (sb * 2 + j) * 512), 16, 0, 0);
+      }
+    };
+    loader(issue, std::integral_constant<int, SW>());
+    return;
+  }
+  if (wave >= 6) {
+    // x: wave 6 + lw copies rows 64 lw .. 64 lw + 63, 8 rows a copy; lane l
+    // loads row 8 i + l / 8, piece (l % 8) ^ swizzle(row), so the LDS holds
+    // the same XOR-swizzled rows as k_gemm4's
+    const int lw = wave - 6;
+    const bf16_t* X = (const bf16_t*)g.x + (size_t)row0 * K;
+    int xoff[8];
+#pragma unroll
+    for (int ii = 0; ii < 8; ++ii) {
+      const int i = lw * 8 + ii;
+      const int row = 8 * i + (lane >> 3);
+      const int piece = (lane & 7) ^ ((row >> 1) & 7);
+      xoff[ii] = (row < xrows ? row : xrows - 1) * K + piece * 8;
+    }
+    auto issue = [&](int t) __attribute__((always_inline)) {
+      const int c = t < nA ? cA + t : t - nA;
+      bf16_t* st = xring + (t % SX) * XST;
+#pragma unroll
+      for (int ii = 0; ii < 8; ++ii)
+        __builtin_amdgcn_global_load_lds((const void*)(X + xoff[ii] + c * KC),
+                                         (lds_void*)(st + (lw * 8 + ii) * 512), 16, 0, 0);
+    };
+    loader(issue, std::integral_constant<int, SX>());
+    return;
+  }
+
+  // ---------------- consumers ----------------
+  const int r = lane & 15, q = lane >> 4;
+  int abase[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) abase[j] = r * 64 + xswz(r, 4 * j + q) * 8;
+  // sums of block bA and of block bA + 1: both pieces leave after the
+  // stream (stores between the weight loads slow the stream down)
+  f32x4_t accA[MT][2], accB[MT][2];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) accA[i][t] = accB[i][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  int sbA, segnA, siA, sbB = 0, segnB = 0, siB = 0;
+  placement(bA, sbA, segnA, siA);
+  const int nlA = bA * NWG - sbA + wave * 32;
+  int nlB = 0;
+  if (n > nA) {
+    placement(bA + 1, sbB, segnB, siB);
+    nlB = (bA + 1) * NWG - sbB + wave * 32;
+  }
+  // fragments of one chunk: A for the MT row tiles, B for the two stripes,
+  // both MFMA steps j
+  U4B fa[MT][2], fb[2][2];
+  auto read_f = [&](int t) __attribute__((always_inline)) {
+    const bf16_t* sw = wring + (t % SW) * WST;
+    const bf16_t* sx = xring + (t % SX) * XST;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+        fb[tt][j].u = *(const u32x4_t*)(sw + ((2 * wave + tt) * 2 + j) * 512 + lane * 8);
+#pragma unroll
+      for (int i = 0; i < MT; ++i) fa[i][j].u = *(const u32x4_t*)(sx + abase[j] + i * 1024);
+    }
+  };
+  // chunk t: barrier t (chunk t is in the rings; every consumer's reads of
+  // chunk t-1 completed before it, so those stages are the loaders' again),
+  // all of chunk t's fragment reads, then its MFMAs: the scheduling
+  // barrier keeps the reads ahead, so a chunk pays one LDS latency
+  auto chunk = [&](int t, f32x4_t (&acc)[MT][2]) __attribute__((always_inline)) {
+    lds_barrier();
+    read_f(t);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        acc[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i][j].v, fb[0][j].v, acc[i][0], 0, 0, 0);
+        acc[i][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i][j].v, fb[1][j].v, acc[i][1], 0, 0, 0);
+      }
+  };
+  for (int t = 0; t < nA; ++t) chunk(t, accA);
+  for (int t = nA; t < n; ++t) chunk(t, accB);
+  lds_barrier();  // barrier n: every consumer done with the rings (the loaders' copies ended before barrier n-1)
+  // a wave's sums -> its park region in the weight ring (rows padded to 36
+  // floats) -> the piece as 128-byte row segments, as in k_gemm4
+  constexpr int PKS = 36;
+  float* pk = (float*)wring + wave * MT * 16 * PKS;
+  auto wave_lds_sync = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  auto park = [&](const f32x4_t (&acc)[MT][2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pk[(i * 16 + 4 * q + e) * PKS + tt * 16 + r] = acc[i][tt][e];
+  };
+  const bool vec_ok = (g.N & 3) == 0;
+  auto store_rows = [&](int slot, int sbase, int segn, int nl) __attribute__((always_inline)) {
+    if (!g.part) return;
+    float* out = g.part + (size_t)slot * g.rows_pad * g.N;
+    const int c4 = (lane & 7) * 4;
+    const int nloc = nl + c4;
+    if (nloc >= segn) return;
+    const int nr = min(MT * 16, g.rows - row0);
+    for (int rr = lane >> 3; rr < nr; rr += 8) {
+      const f32x4_t v = *(const f32x4_t*)(pk + rr * PKS + c4);
+      float* dst = out + (size_t)(row0 + rr) * g.N + sbase + nloc;
+      if (vec_ok && nloc + 3 < segn) {
+        __builtin_nontemporal_store(v, (f32x4_t*)dst);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (nloc + k < segn) dst[k] = v[k];
+      }
+    }
+  };
+  // block bA's piece goes to its slot among the block's pieces; block
+  // bA + 1 starts with this run, so its piece is slot 0
+  const int slotA = wg - plan_first_wg(g.sp, bA);
+  park(accA);
+  wave_lds_sync();
+  store_rows(slotA, sbA, segnA, nlA);
+  if (n > nA) {
+    wave_lds_sync();
+    park(accB);
+    wave_lds_sync();
+    store_rows(0, sbB, segnB, nlB);
+  }
+}
+
 // fp32 models: one wave per output element.  Lane l sums k = l, l + 64, ...
 // in order, then the 64 lane sums are added by a fixed xor-shuffle tree, so
 // an element's sum does not depend on the row count; the lanes read the
@@ -698,9 +932,15 @@ hipError_t launch_gemm(const GemmDesc& g, int dtype, hipStream_t st) {
   dim3 grid(g.sp.G, 1, mblk);
   // one row tile (the autoregressive step): the producer-wave kernel, which
   // streams fastest when the MFMA work is small; more rows: the four-wave
-  // kernel.  Both accumulate every output element over the same chunks in
-  // the same MFMA order, so a row's sums do not depend on which one ran.
+  // kernel, or for 8 row tiles and runs of at most 22 chunks a workgroup on
+  // average, the loader / consumer kernel (measured faster there, slower on
+  // longer runs).  All accumulate every output element over the same chunks
+  // in the same MFMA order, so a row's sums do not depend on which one ran.
   const dim3 b4(256);
+  if (mt == 8 && !g.amax_keys && (long long)g.sp.nblk * g.sp.nch <= 22LL * g.sp.G) {
+    la_launch(k_gemm_dma<8>, grid, dim3(512), 0, st, g);
+    return hipGetLastError();
+  }
   switch (mt) {
     case 1: la_launch(k_gemm_bf16<1>, grid, dim3(320), 0, st, g); break;
     case 2: la_launch(k_gemm4<2>, grid, b4, 0, st, g); break;

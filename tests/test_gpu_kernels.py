@@ -72,7 +72,7 @@ def test_pack_layout(N, K):
 
 @pytest.mark.parametrize("M,K,N", [(1, 256, 384), (17, 512, 640), (121, 4096, 4096),
                                    (121, 1024, 1000), (300, 512, 256), (121, 11008, 4096),
-                                   (121, 4096, 32000)])
+                                   (121, 1344, 1000), (121, 4096, 32000)])
 def test_gemm_bf16_matches_definition(M, K, N):
     print(f"gemm M={M} K={K} N={N}", flush=True)
     rng = np.random.default_rng(M * 7 + K + N)
@@ -95,12 +95,16 @@ def test_gemm_f32_matches_definition():
     assert np.abs(y - ref).max() < 1e-4
 
 
-def test_gemm_rows_bit_identical_across_batch():
+@pytest.mark.parametrize("K,N", [(4096, 4096), (11008, 4096), (4096, 12288)])
+def test_gemm_rows_bit_identical_across_batch(K, N):
     """A row's output bits do not depend on how many rows share the call or
     where the row sits (what makes lookahead rows reproduce the
-    autoregressive step)."""
+    autoregressive step).  At 121 rows the first two shapes run the
+    loader / consumer kernel (the second with runs that cross a column
+    block), the third the four-wave kernel; one row runs the producer-wave
+    kernel and 17 rows the four-wave kernel with two row tiles."""
+    print(f"gemm bit identity K={K} N={N}", flush=True)
     rng = np.random.default_rng(11)
-    K, N = 4096, 4096
     x = _bf16(rng.standard_normal((121, K)))
     w = _bf16(rng.standard_normal((N, K)) * 0.02)
     wp = _pack(w)
