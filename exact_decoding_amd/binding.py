@@ -18,7 +18,7 @@ LA_OK, LA_DONE = 0, 1
 LA_EINVAL, LA_ENOMEM, LA_ECTX, LA_EHIP, LA_ESTATE = -1, -2, -3, -4, -5
 LA_F32, LA_BF16 = 0, 1
 LA_MAX_N = 16
-LA_PROBE_BLOCKS = 2048
+LA_PROBE_BLOCKS = 256
 LA_NOALLOC_SCRATCH_BYTES = 32 << 20
 LA_PROMPT_REF, LA_AR, LA_NO_GRAPH, LA_POOL_LRU, LA_POOL_CONTEXT = 1, 2, 8, 16, 32
 LA_ADAPTIVE_G, LA_DEBUG_LOGITS = 64, 4

@@ -774,18 +774,38 @@ __global__ void k_fill_i32(int32_t* p, int32_t v, size_t n) {
   if (i < n) p[i] = v;
 }
 
-// Streaming read: every thread XORs 16-byte words with a grid stride; the
-// per-block XOR goes to out[block] so the loads are not dead.
+// Streaming read: wave w of the grid XORs the 16-byte words of slice w
+// (ceil(n16 / waves) rounded up to whole 1 KB wave-loads; the last slices may
+// be short or empty); the per-block XOR goes to out[block] so the loads are
+// not dead.
 __global__ __launch_bounds__(256) void k_probe_read(const uint4* __restrict__ buf, size_t n16,
                                                     uint32_t* out) {
+  // each wave streams one contiguous slice of 1 KB wave-loads (16 bytes a
+  // lane, non-temporal) and keeps PD of them in flight: a load is reissued
+  // as soon as its value has been folded into the checksum
+  typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+  constexpr int PD = 32;
+  const int lane = threadIdx.x & 63;
+  const size_t waves = (size_t)gridDim.x * 4;
+  const size_t w = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const size_t per = ((n16 + waves - 1) / waves + 63) / 64 * 64;
+  const size_t lo = w * per;
+  const size_t hi = lo + per < n16 ? lo + per : n16;
+  const size_t nk = hi > lo ? (hi - lo + 63) / 64 : 0;  // wave-loads of this slice
+  auto load = [&](size_t k) -> u4v {
+    const size_t j = lo + k * 64 + lane;
+    return k < nk && j < hi ? __builtin_nontemporal_load((const u4v*)(buf + j)) : u4v{0u, 0u, 0u, 0u};
+  };
+  u4v r[PD];
+#pragma unroll
+  for (int u = 0; u < PD; ++u) r[u] = load(u);
   uint32_t acc = 0;
-  const size_t stride = (size_t)gridDim.x * 256 * 4;
-  for (size_t i = (size_t)blockIdx.x * 256 * 4 + threadIdx.x; i < n16; i += stride) {
-    uint4 v[4];
+  for (size_t k0 = 0; k0 < nk; k0 += PD) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = i + u * 256 < n16 ? buf[i + u * 256] : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    for (int u = 0; u < PD; ++u) {
+      acc ^= r[u].x ^ r[u].y ^ r[u].z ^ r[u].w;
+      r[u] = load(k0 + PD + u);
+    }
   }
   __shared__ uint32_t red[256];
   red[threadIdx.x] = acc;

@@ -342,10 +342,11 @@ int la_kernel_gemm_noalloc(const void* x, int32_t M, int32_t K, const void* w, i
 int la_philox_uniform(uint64_t seed, uint64_t step, int32_t n, float* out, void* hip_stream);
 
 /* HBM read probe (benchmark hook): reads `bytes` (a multiple of 16) from the
- * device buffer `buf` with 16-byte loads across the whole chip and writes one
+ * device buffer `buf` across the whole chip (each wave one contiguous slice,
+ * 16-byte non-temporal loads, 32 KB in flight per wave) and writes one XOR
  * checksum word per workgroup to `out` (device, LA_PROBE_BLOCKS uint32);
  * measures the achievable read bandwidth.  Enqueued on `hip_stream`. */
-#define LA_PROBE_BLOCKS 2048
+#define LA_PROBE_BLOCKS 256
 int la_probe_read(const void* buf, size_t bytes, uint32_t* out, void* hip_stream);
 
 #ifdef __cplusplus

@@ -95,6 +95,28 @@ def test_gemm_f32_matches_definition():
     assert np.abs(y - ref).max() < 1e-4
 
 
+@pytest.mark.parametrize("nbytes", [16, 1024 * 1024, 1024 * 1024 + 48, 5 * 1024 * 1024 + 16 * 333])
+def test_probe_read_checksums(nbytes):
+    """la_probe_read reads every byte once: workgroup b's word is the XOR of the
+    32-bit words of its four waves' slices (whole 1 KB wave-loads, the tail
+    short or empty)."""
+    rng = np.random.default_rng(nbytes)
+    host = rng.integers(0, 2**32, size=nbytes // 4, dtype=np.uint64).astype(np.uint32)
+    buf = torch.from_numpy(host.view(np.uint8).copy()).to(DEV)
+    out = torch.zeros(B.LA_PROBE_BLOCKS, dtype=torch.int32, device=DEV)
+    B.la_probe_read(buf, nbytes, out, None)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint32)
+    n16 = nbytes // 16
+    waves = B.LA_PROBE_BLOCKS * 4
+    per = ((n16 + waves - 1) // waves + 63) // 64 * 64
+    words = host.reshape(-1, 4)
+    for b in range(B.LA_PROBE_BLOCKS):
+        lo, hi = min(4 * b * per, n16), min((4 * b + 4) * per, n16)
+        want = np.bitwise_xor.reduce(words[lo:hi].ravel()) if hi > lo else np.uint32(0)
+        assert got[b] == want, (b, lo, hi)
+
+
 @pytest.mark.parametrize("K,N", [(4096, 4096), (11008, 4096), (4096, 12288)])
 def test_gemm_rows_bit_identical_across_batch(K, N):
     """A row's output bits do not depend on how many rows share the call or
