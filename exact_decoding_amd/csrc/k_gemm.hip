@@ -600,7 +600,7 @@ void k_gemm4(GemmDesc g) {
   }
 }
 
-// Loader / consumer form of the multi-row kernel, for 8 row tiles and
+// Loader / consumer form of the multi-row kernel, for MT row tiles and
 // short runs (no argmax keys).  Eight waves:
 //  * waves 4-5 copy each chunk's weights (one contiguous 16 KB unit of the
 //    packed layout) into a ring of SW LDS stages, SW-1 chunks ahead;
@@ -616,7 +616,8 @@ void k_gemm4(GemmDesc g) {
 // ends: stores between the weight loads slow the stream down.
 // Measured against k_gemm4 inside the 7B and 13B steps, this form ends a
 // run of up to ~22 chunks sooner (its loaders are SW-1 chunks ahead from
-// the first instruction) but streams the long runs more slowly.
+// the first instruction) but streams the long runs more slowly; at 2-4 row
+// tiles it is the slower one throughout.
 typedef __attribute__((address_space(3))) void lds_void;
 // s_waitcnt immediate for vmcnt(v) alone (gfx9 bit layout)
 __device__ constexpr int vmcnt_imm(int v) { return (v & 15) | ((v >> 4) << 14) | 0x70 | 0xF00; }
@@ -626,7 +627,7 @@ void k_gemm_dma(GemmDesc g) {
   constexpr int SW = 7, SX = 3;  // weight and x stages
   constexpr int WST = 8 * 1024;           // bf16 of one weight unit (8 stripes x 2 KB)
   constexpr int XST = MT * 16 * 64;       // bf16 of one x tile
-  static_assert(MT == 8, "two x loader waves copy 8 KB each");
+  static_assert(MT >= 2 && MT <= 8, "two x loader waves copy MT KB each");
   static_assert((SW * WST + SX * XST) * 2 <= 160 * 1024, "LDS");
   static_assert(SW * WST * 2 >= 4 * MT * 16 * 36 * 4, "the park reuses the weight ring");
   __shared__ __align__(16) bf16_t wring[SW * WST];
@@ -651,15 +652,16 @@ void k_gemm_dma(GemmDesc g) {
     while (si < g.nseg - 1 && col0 >= sbase + g.seg[si].n) { sbase += g.seg[si].n; ++si; }
     segn = g.seg[si].n;
   };
-  // loader loop (each loader wave issues 8 copies a chunk): wait for chunk
-  // t (younger chunks t+1 .. t+S-2 may fly), barrier t, then chunk t+S-1
+  // loader loop (a loader wave issues C copies a chunk): wait for chunk t
+  // (younger chunks t+1 .. t+S-2 may fly), barrier t, then chunk t+S-1
   // into the stage chunk t-1 left
-  auto loader = [&](auto issue, auto s_tag) __attribute__((always_inline)) {
+  auto loader = [&](auto issue, auto s_tag, auto c_tag) __attribute__((always_inline)) {
     constexpr int S = decltype(s_tag)::value;
+    constexpr int C = decltype(c_tag)::value;
     for (int t = 0; t < S - 1 && t < n; ++t) issue(t);
     for (int t = 0; t < n; ++t) {
       if (t + S - 2 <= n - 1)
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 2) * 8));
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 2) * C));
       else
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       lds_barrier();
@@ -698,19 +700,19 @@ void k_gemm_dma(GemmDesc g) {
                                            (lds_void*)(st + (sb * 2 + j) * 512), 16, 0, 0);
       }
     };
-    loader(issue, std::integral_constant<int, SW>());
+    loader(issue, std::integral_constant<int, SW>(), std::integral_constant<int, 8>());
     return;
   }
   if (wave >= 6) {
-    // x: wave 6 + lw copies rows 64 lw .. 64 lw + 63, 8 rows a copy; lane l
-    // loads row 8 i + l / 8, piece (l % 8) ^ swizzle(row), so the LDS holds
-    // the same XOR-swizzled rows as k_gemm4's
+    // x: wave 6 + lw copies rows 8 MT lw .. 8 MT lw + 8 MT - 1, 8 rows a
+    // copy; lane l loads row 8 i + l / 8, piece (l % 8) ^ swizzle(row), so
+    // the LDS holds the same XOR-swizzled rows as k_gemm4's
     const int lw = wave - 6;
     const bf16_t* X = (const bf16_t*)g.x + (size_t)row0 * K;
-    int xoff[8];
+    int xoff[MT];
 #pragma unroll
-    for (int ii = 0; ii < 8; ++ii) {
-      const int i = lw * 8 + ii;
+    for (int ii = 0; ii < MT; ++ii) {
+      const int i = lw * MT + ii;
       const int row = 8 * i + (lane >> 3);
       const int piece = (lane & 7) ^ ((row >> 1) & 7);
       xoff[ii] = (row < xrows ? row : xrows - 1) * K + piece * 8;
@@ -719,11 +721,11 @@ void k_gemm_dma(GemmDesc g) {
       const int c = t < nA ? cA + t : t - nA;
       bf16_t* st = xring + (t % SX) * XST;
 #pragma unroll
-      for (int ii = 0; ii < 8; ++ii)
+      for (int ii = 0; ii < MT; ++ii)
         __builtin_amdgcn_global_load_lds((const void*)(X + xoff[ii] + c * KC),
-                                         (lds_void*)(st + (lw * 8 + ii) * 512), 16, 0, 0);
+                                         (lds_void*)(st + (lw * MT + ii) * 512), 16, 0, 0);
     };
-    loader(issue, std::integral_constant<int, SX>());
+    loader(issue, std::integral_constant<int, SX>(), std::integral_constant<int, MT>());
     return;
   }
 
@@ -932,13 +934,18 @@ hipError_t launch_gemm(const GemmDesc& g, int dtype, hipStream_t st) {
   dim3 grid(g.sp.G, 1, mblk);
   // one row tile (the autoregressive step): the producer-wave kernel, which
   // streams fastest when the MFMA work is small; more rows: the four-wave
-  // kernel, or for 8 row tiles and runs of at most 22 chunks a workgroup on
-  // average, the loader / consumer kernel (measured faster there, slower on
-  // longer runs).  All accumulate every output element over the same chunks
-  // in the same MFMA order, so a row's sums do not depend on which one ran.
+  // kernel, or for 6-8 row tiles and runs of at most 22 chunks a workgroup
+  // on average, the loader / consumer kernel (measured faster there, slower
+  // on longer runs and at 2-4 row tiles).  All accumulate every output
+  // element over the same chunks in the same MFMA order, so a row's sums do
+  // not depend on which one ran.
   const dim3 b4(256);
-  if (mt == 8 && !g.amax_keys && (long long)g.sp.nblk * g.sp.nch <= 22LL * g.sp.G) {
-    la_launch(k_gemm_dma<8>, grid, dim3(512), 0, st, g);
+  if (mt >= 6 && !g.amax_keys && (long long)g.sp.nblk * g.sp.nch <= 22LL * g.sp.G) {
+    switch (mt) {
+      case 6: la_launch(k_gemm_dma<6>, grid, dim3(512), 0, st, g); break;
+      case 7: la_launch(k_gemm_dma<7>, grid, dim3(512), 0, st, g); break;
+      default: la_launch(k_gemm_dma<8>, grid, dim3(512), 0, st, g); break;
+    }
     return hipGetLastError();
   }
   switch (mt) {
